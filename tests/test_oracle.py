@@ -1,0 +1,244 @@
+"""Pins for the fp64 oracle (CPU only).
+
+The oracle is checked against things other than itself: an explicit
+dense-transition brute force, closed forms, textbook special cases, the
+chunk (WY) algebra computed separately in fp64, invariants of the
+recurrence (split = chain, linearity), and the page's worked chunk-table
+example.  Non-square key/value sizes (dk != dv) make a transposed operand
+fail loudly.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_inputs(rng, lengths, H, dk, dv, h0=True, gscale=5.0):
+    lengths = list(lengths)
+    T = int(sum(lengths))
+    N = len(lengths)
+    cu = np.zeros(N + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    q = rng.standard_normal((T, H, dk)).astype(np.float32) / np.float32(math.sqrt(dk))
+    k = rng.standard_normal((T, H, dk)).astype(np.float32)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True).astype(np.float32)
+    v = rng.standard_normal((T, H, dv)).astype(np.float32)
+    g = (-gscale / (1.0 + np.exp(-rng.standard_normal((T, H, dk))))).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((T, H))))).astype(np.float32)
+    S0 = (0.1 * rng.standard_normal((N, H, dk, dv))).astype(np.float32) if h0 else None
+    return q, k, v, g, beta, cu, S0
+
+
+def rel(a, b):
+    return oracle.rel_fro_err(a, b)
+
+
+@pytest.mark.parametrize("dk,dv", [(8, 6), (5, 9), (128, 128)])
+def test_token_oracle_matches_dense_brute_force(dk, dv):
+    rng = np.random.default_rng(11)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [13, 0, 19], H=2, dk=dk, dv=dv)
+    o, fin = oracle.kda_fwd(q, k, v, g, beta, cu, S0, scale=0.7)
+    ob, fb = oracle.brute_force(q, k, v, g, beta, cu, S0, scale=0.7)
+    assert rel(o, ob) < 1e-12
+    assert rel(fin, fb) < 1e-12
+
+
+def test_token_oracle_brute_force_without_initial_state():
+    rng = np.random.default_rng(12)
+    q, k, v, g, beta, cu, _ = rand_inputs(rng, [32], H=3, dk=16, dv=12, h0=False)
+    o, fin = oracle.kda_fwd(q, k, v, g, beta, cu, None)
+    ob, fb = oracle.brute_force(q, k, v, g, beta, cu, None)
+    assert rel(o, ob) < 1e-12 and rel(fin, fb) < 1e-12
+
+
+def test_beta_zero_is_pure_decay_closed_form():
+    rng = np.random.default_rng(13)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [40, 7, 0, 25], H=2, dk=16, dv=10)
+    beta[:] = 0.0
+    o, fin = oracle.kda_fwd(q, k, v, g, beta, cu, S0)
+    oc, fc = oracle.decay_closed_form(q, g, cu, S0)
+    assert rel(o, oc) < 1e-12
+    assert rel(fin, fc) < 1e-12
+
+
+def test_beta_zero_g_zero_is_a_plain_readout():
+    # g = 0 and beta = 0: the state is frozen, o_t = scale * S_0^T q_t.
+    rng = np.random.default_rng(14)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [30], H=1, dk=12, dv=7)
+    g[:] = 0.0
+    beta[:] = 0.0
+    o, fin = oracle.kda_fwd(q, k, v, g, beta, cu, S0, scale=0.5)
+    expect = 0.5 * q[:, 0].astype(np.float64) @ S0[0, 0].astype(np.float64)
+    assert np.max(np.abs(o[:, 0] - expect)) < 1e-13
+    assert np.array_equal(fin[0, 0], S0[0, 0].astype(np.float64))
+
+
+def test_orthonormal_keys_reduce_to_causal_linear_attention():
+    rng = np.random.default_rng(15)
+    T, dk, dv = 24, 32, 20
+    q, _, v, _, beta, cu, _ = rand_inputs(rng, [T], H=2, dk=dk, dv=dv, h0=False)
+    k = np.zeros((T, 2, dk), dtype=np.float64)
+    for h in range(2):
+        Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+        k[:, h] = Qm[:, :T].T                         # T orthonormal keys
+    g = np.zeros((T, 2, dk), dtype=np.float32)
+    o, _ = oracle.kda_fwd(q, k, v, g, beta, cu, None)
+    ol = oracle.linear_attention(q, k, v, beta)
+    # k went through fp32 on its way into the oracle; compare against the
+    # same fp32 keys.
+    ol32 = oracle.linear_attention(q, k.astype(np.float32), v, beta)
+    assert rel(o, ol32) < 1e-6
+    assert rel(ol, ol32) < 1e-6
+
+
+def test_one_hot_key_with_unit_beta_overwrites_the_slot():
+    # g = 0, beta = 1, k = e_i: S[i,:] is replaced by v_t, other rows kept.
+    rng = np.random.default_rng(16)
+    dk, dv, T = 6, 5, 9
+    slots = rng.integers(0, dk, size=T)
+    k = np.zeros((T, 1, dk), dtype=np.float32)
+    k[np.arange(T), 0, slots] = 1.0
+    q = rng.standard_normal((T, 1, dk)).astype(np.float32)
+    v = rng.standard_normal((T, 1, dv)).astype(np.float32)
+    g = np.zeros((T, 1, dk), dtype=np.float32)
+    beta = np.ones((T, 1), dtype=np.float32)
+    S0 = rng.standard_normal((1, 1, dk, dv)).astype(np.float32)
+    cu = np.array([0, T], dtype=np.int32)
+    o, fin = oracle.kda_fwd(q, k, v, g, beta, cu, S0, scale=1.0)
+    S = S0[0, 0].astype(np.float64).copy()
+    for t in range(T):
+        S[slots[t]] = v[t, 0]
+        assert np.allclose(o[t, 0], S.T @ q[t, 0].astype(np.float64), atol=1e-12)
+    assert np.allclose(fin[0, 0], S, atol=1e-12)
+
+
+def test_split_equals_chain_bitwise():
+    rng = np.random.default_rng(17)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [150], H=2, dk=16, dv=8)
+    o, fin = oracle.kda_fwd(q, k, v, g, beta, cu, S0)
+    cut = 67
+    cuA = np.array([0, cut], dtype=np.int32)
+    cuB = np.array([0, 150 - cut], dtype=np.int32)
+    oA, fA = oracle.kda_fwd(q[:cut], k[:cut], v[:cut], g[:cut], beta[:cut], cuA, S0)
+    # the chained call gets the fp64 state; feed it through float64 inputs
+    # by running the brute force free variant: compare against the packed
+    # run of [A;B] as two sequences with B's initial state = fA.
+    cu2 = np.array([0, cut, 150], dtype=np.int32)
+    h2 = np.concatenate([S0, fA.astype(np.float32)], axis=0)
+    o2, f2 = oracle.kda_fwd(q, k, v, g, beta, cu2, h2)
+    assert np.array_equal(o2[:cut], oA)
+    assert np.array_equal(o[:cut], oA)
+    # second half: bitwise equal to a standalone run from the same state
+    oB, fB = oracle.kda_fwd(q[cut:], k[cut:], v[cut:], g[cut:], beta[cut:], cuB,
+                            fA.astype(np.float32))
+    assert np.array_equal(o2[cut:], oB)
+    assert np.array_equal(f2[1], fB[0])
+    # and, up to the fp32 rounding of the handed-over state, the full run
+    assert rel(oB, o[cut:]) < 1e-6 and rel(fB, fin) < 1e-6
+
+
+def test_packing_order_and_neighbours_do_not_matter():
+    rng = np.random.default_rng(18)
+    lens = [33, 0, 70, 5]
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, lens, H=2, dk=8, dv=8)
+    o, fin = oracle.kda_fwd(q, k, v, g, beta, cu, S0)
+    for s in range(len(lens)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        cus = np.array([0, b - a], dtype=np.int32)
+        os_, fs = oracle.kda_fwd(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], cus,
+                                 S0[s:s + 1])
+        assert np.array_equal(o[a:b], os_)
+        assert np.array_equal(fin[s], fs[0])
+    # empty sequence: final_state = initial_state, bitwise
+    assert np.array_equal(fin[1], S0[1].astype(np.float64))
+
+
+def test_linear_in_values_and_initial_state():
+    rng = np.random.default_rng(19)
+    q, k, v1, g, beta, cu, S1 = rand_inputs(rng, [45, 20], H=2, dk=12, dv=10)
+    v2 = rng.standard_normal(v1.shape).astype(np.float32)
+    S2 = rng.standard_normal(S1.shape).astype(np.float32)
+    a = 0.75
+    o1, f1 = oracle.kda_fwd(q, k, v1, g, beta, cu, S1)
+    o2, f2 = oracle.kda_fwd(q, k, v2, g, beta, cu, S2)
+    vm = (a * v1.astype(np.float64) + v2).astype(np.float32)
+    Sm = (a * S1.astype(np.float64) + S2).astype(np.float32)
+    om, fm = oracle.kda_fwd(q, k, vm, g, beta, cu, Sm)
+    # the fp32 rounding of the mixed inputs bounds the agreement
+    assert rel(om, a * o1 + o2) < 1e-6
+    assert rel(fm, a * f1 + f2) < 1e-6
+
+
+@pytest.mark.parametrize("lens", [[130, 64, 210], [53, 14, 13, 33, 16, 8, 1, 77]])
+def test_chunked_form_matches_token_form(lens):
+    rng = np.random.default_rng(20)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, lens, H=2, dk=16, dv=12)
+    g[:, :, :3] = -5.0                                # pinned lower bound
+    o, fin = oracle.kda_fwd(q, k, v, g, beta, cu, S0)
+    oc, fc = oracle.chunked_fwd(q, k, v, g, beta, cu, S0, bt=64)
+    assert rel(oc, o) < 1e-12
+    assert rel(fc, fin) < 1e-12
+    oc16, fc16 = oracle.chunked_fwd(q, k, v, g, beta, cu, S0, bt=16)
+    assert rel(oc16, o) < 1e-12 and rel(fc16, fin) < 1e-12
+
+
+def test_chunked_form_at_full_head_size():
+    rng = np.random.default_rng(21)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [200], H=1, dk=128, dv=128)
+    o, fin = oracle.kda_fwd(q, k, v, g, beta, cu, S0)
+    oc, fc = oracle.chunked_fwd(q, k, v, g, beta, cu, S0)
+    assert rel(oc, o) < 1e-12 and rel(fc, fin) < 1e-12
+
+
+def test_chunk_table_matches_page_example():
+    with open(os.path.join(GOLDEN, "chunk_table_70_130.json")) as f:
+        gold = json.load(f)
+    lens = gold["lengths"]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    rows = oracle.chunk_table(cu, bt=gold["chunk_size"])
+    assert [[r["seq"], r["local"]] for r in rows] == gold["chunk_indices"]
+    assert [r["aligned_start"] for r in rows] == gold["starts"]
+    aligned = [((L + 63) // 64) * 64 for L in lens]
+    assert aligned == gold["aligned_lengths"]
+    assert list(np.concatenate([[0], np.cumsum(aligned)])) == gold["aligned_cu_seqlens"]
+    assert [r["start_flag"] for r in rows] == [1, 0, 1, 0, 0]
+    assert [r["end_flag"] for r in rows] == [0, 1, 0, 0, 1]
+    assert [r["start"] for r in rows] == [0, 64, 70, 134, 198]
+    assert [r["length"] for r in rows] == [64, 6, 64, 64, 2]
+
+
+def test_chunk_table_empty_and_exact_multiples():
+    cu = np.array([0, 0, 64, 64, 192, 193], dtype=np.int32)
+    rows = oracle.chunk_table(cu)
+    assert [r["seq"] for r in rows] == [1, 3, 3, 4]
+    assert [r["length"] for r in rows] == [64, 64, 64, 1]
+    assert [(r["start_flag"], r["end_flag"]) for r in rows] == [(1, 1), (1, 0), (0, 1), (1, 1)]
+
+
+def test_strip_exponent_budget_reached_at_the_lower_bound():
+    # All gates at the lower bound -5: the subblock-midpoint reference keeps
+    # every factor within 8 steps * 5 = 40 nats, i.e. 57.7 bits < 126.
+    g = np.full((64, 4), -5.0)
+    worst = oracle.strip_exponents(g)
+    assert worst == pytest.approx(40.0)
+    assert worst / math.log(2.0) == pytest.approx(57.7, abs=0.05)
+    assert worst / math.log(2.0) < 126
+    rng = np.random.default_rng(22)
+    g = -5.0 / (1.0 + np.exp(-rng.standard_normal((64, 128))))
+    assert oracle.strip_exponents(g) < 40.0
+    # a partial last chunk clamps the reference row and stays in budget
+    assert oracle.strip_exponents(np.full((37, 2), -5.0)) <= 40.0
+
+
+def test_error_metrics():
+    a = np.array([1.0, 2.0, 2.0])
+    b = np.array([1.0, 2.0, 3.0])
+    assert oracle.max_abs_err(a, b) == 1.0
+    assert oracle.rel_fro_err(a, b) == pytest.approx(1.0 / math.sqrt(14.0))
