@@ -1,0 +1,20 @@
+"""MI355X-native Kimi Delta Attention (KDA) chunked prefill, forward pass.
+
+The compute lives in hand-written HIP kernels for gfx950 behind the C ABI of
+``libkda.so`` (include/kda.h); this package only marshals arguments.  The
+library is loaded on first use and its absence is an error.
+"""
+
+from ._binding import (  # noqa: F401
+    EXPORTED,
+    KDAError,
+    LIB_PATH,
+    chunk_fwd,
+    chunk_intra,
+    chunk_table,
+    gate_cumsum,
+    load_library,
+    new_workspace,
+    workspace_layout,
+    workspace_size,
+)

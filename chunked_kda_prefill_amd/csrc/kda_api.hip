@@ -1,0 +1,209 @@
+// C ABI of libkda: argument validation on the host, then kernel launches on
+// the caller's stream.  Nothing here reads device memory, allocates, or
+// synchronises.
+#include "../../include/kda.h"
+#include "kda_internal.h"
+#include "kda_launch.h"
+
+#include <stdint.h>
+
+using namespace kda;
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [p, p + bytes) and [q, q + qbytes) overlap?
+bool overlap(const void *p, int64_t bytes, const void *q, int64_t qbytes) {
+  if (!p || !q || bytes <= 0 || qbytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + (uintptr_t)bytes;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(q), b1 = b0 + (uintptr_t)qbytes;
+  return a0 < b1 && b0 < a1;
+}
+
+kda_status check_sizes(int64_t T, int32_t N, int32_t H) {
+  if (T < 0 || N < 1 || H < 1) return KDA_ERR_INVALID_ARGUMENT;
+  if (T > INT32_MAX || H > 65535) return KDA_ERR_UNSUPPORTED;
+  const int64_t nc_max = nc_max_of(T, N);
+  // grids are 1-D: (chunk slots x heads) and (chains / 8 x 32) workgroups
+  if (nc_max * (int64_t)H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if (((int64_t)N * H + 7) / 8 * 32 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  return KDA_OK;
+}
+
+struct Ws {
+  WsLayout L;
+  int32_t *flags;
+  int32_t *chunk_first;
+  int4 *chunk_info;
+  uint8_t *blocks;
+};
+
+kda_status carve(void *workspace, size_t workspace_bytes, int64_t T, int32_t N, int32_t H,
+                 Ws &ws) {
+  if (!workspace) return KDA_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 256)) return KDA_ERR_INVALID_ARGUMENT;
+  ws.L = ws_layout(T, N, H);
+  if ((int64_t)workspace_bytes < ws.L.total) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  uint8_t *base = static_cast<uint8_t *>(workspace);
+  ws.flags = reinterpret_cast<int32_t *>(base + ws.L.off_flags);
+  ws.chunk_first = reinterpret_cast<int32_t *>(base + ws.L.off_chunk_first);
+  ws.chunk_info = reinterpret_cast<int4 *>(base + ws.L.off_chunk_info);
+  ws.blocks = base + ws.L.off_blocks;
+  return KDA_OK;
+}
+
+kda_status check_inputs(const void *q, const void *k, const void *v, const float *g,
+                        const float *beta, const int32_t *cu, int64_t T) {
+  if (!cu || !aligned(cu, 4)) return KDA_ERR_INVALID_ARGUMENT;
+  if (T > 0) {
+    if (!q || !k || !v || !g || !beta) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) ||
+        !aligned(beta, 4))
+      return KDA_ERR_INVALID_ARGUMENT;
+  }
+  return KDA_OK;
+}
+
+kda_status hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "KDA_ERR_WORKSPACE_TOO_SMALL";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+size_t kda_chunk_fwd_workspace_size(int64_t T, int32_t N, int32_t H) {
+  if (check_sizes(T, N, H) != KDA_OK) return 0;
+  return (size_t)ws_layout(T, N, H).total;
+}
+
+kda_status kda_workspace_layout(int64_t T, int32_t N, int32_t H, int64_t out[5]) {
+  if (!out) return KDA_ERR_INVALID_ARGUMENT;
+  const kda_status st = check_sizes(T, N, H);
+  if (st != KDA_OK) return st;
+  const WsLayout L = ws_layout(T, N, H);
+  out[0] = L.off_flags;
+  out[1] = L.off_chunk_first;
+  out[2] = L.off_chunk_info;
+  out[3] = L.off_blocks;
+  out[4] = BLOCK_BYTES;
+  return KDA_OK;
+}
+
+kda_status kda_chunk_table(const int32_t *cu_seqlens, int64_t T, int32_t N, int32_t *chunk_first,
+                           int32_t *chunk_info, int32_t *flags, hipStream_t stream) {
+  kda_status st = check_sizes(T, N, 1);
+  if (st != KDA_OK) return st;
+  if (!cu_seqlens || !chunk_first || !chunk_info || !flags) return KDA_ERR_INVALID_ARGUMENT;
+  if (!aligned(cu_seqlens, 4) || !aligned(chunk_first, 4) || !aligned(chunk_info, 16) ||
+      !aligned(flags, 4))
+    return KDA_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_chunk_table(cu_seqlens, T, N, nc_max_of(T, N), chunk_first,
+                                       reinterpret_cast<int4 *>(chunk_info), flags, stream));
+}
+
+kda_status kda_gate_cumsum(const float *g, const int32_t *cu_seqlens, int64_t T, int32_t N,
+                           int32_t H, float *G, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  kda_status st = check_sizes(T, N, H);
+  if (st != KDA_OK) return st;
+  if (!cu_seqlens || !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!g || !G || !aligned(g, 16) || !aligned(G, 16))) return KDA_ERR_INVALID_ARGUMENT;
+  if (overlap(G, T * H * DK * 4, g, T * H * DK * 4)) return KDA_ERR_INVALID_ARGUMENT;
+  Ws ws;
+  if ((st = carve(workspace, workspace_bytes, T, N, H, ws)) != KDA_OK) return st;
+  hipError_t e = launch_chunk_table(cu_seqlens, T, N, ws.L.nc_max, ws.chunk_first, ws.chunk_info,
+                                    ws.flags, stream);
+  if (e != hipSuccess) return KDA_ERR_HIP;
+  return hip_status(
+      launch_gate_cumsum(g, ws.chunk_first, ws.chunk_info, ws.L.nc_max, N, H, G, stream));
+}
+
+static kda_status run_intra(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const int32_t *cu_seqlens, int64_t T, int32_t N,
+                            int32_t H, float scale, const Ws &ws, hipStream_t stream) {
+  hipError_t e = launch_chunk_table(cu_seqlens, T, N, ws.L.nc_max, ws.chunk_first, ws.chunk_info,
+                                    ws.flags, stream);
+  if (e != hipSuccess) return KDA_ERR_HIP;
+  IntraArgs ia;
+  ia.q = static_cast<const uint16_t *>(q);
+  ia.k = static_cast<const uint16_t *>(k);
+  ia.v = static_cast<const uint16_t *>(v);
+  ia.g = g;
+  ia.beta = beta;
+  ia.chunk_first = ws.chunk_first;
+  ia.chunk_info = ws.chunk_info;
+  ia.blocks = ws.blocks;
+  ia.nc_max = ws.L.nc_max;
+  ia.N = N;
+  ia.H = H;
+  ia.scale = scale;
+  return hip_status(launch_intra(ia, stream));
+}
+
+kda_status kda_chunk_intra(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const int32_t *cu_seqlens, int64_t T, int32_t N,
+                           int32_t H, float scale, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  kda_status st = check_sizes(T, N, H);
+  if (st != KDA_OK) return st;
+  if ((st = check_inputs(q, k, v, g, beta, cu_seqlens, T)) != KDA_OK) return st;
+  Ws ws;
+  if ((st = carve(workspace, workspace_bytes, T, N, H, ws)) != KDA_OK) return st;
+  return run_intra(q, k, v, g, beta, cu_seqlens, T, N, H, scale, ws, stream);
+}
+
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                         int64_t T, int32_t N, int32_t H, float scale, void *o,
+                         float *final_state, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  kda_status st = check_sizes(T, N, H);
+  if (st != KDA_OK) return st;
+  if ((st = check_inputs(q, k, v, g, beta, cu_seqlens, T)) != KDA_OK) return st;
+  if (T > 0 && (!o || !aligned(o, 16))) return KDA_ERR_INVALID_ARGUMENT;
+  if ((initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
+    return KDA_ERR_INVALID_ARGUMENT;
+  const int64_t tok = T * H * DK;
+  const int64_t st_bytes = (int64_t)N * H * DK * DV * 4;
+  // o must not alias any input; final_state may only alias initial_state exactly
+  if (overlap(o, tok * 2, q, tok * 2) || overlap(o, tok * 2, k, tok * 2) ||
+      overlap(o, tok * 2, v, tok * 2) || overlap(o, tok * 2, g, tok * 4) ||
+      overlap(o, tok * 2, beta, T * H * 4) || overlap(o, tok * 2, final_state, st_bytes) ||
+      overlap(o, tok * 2, initial_state, st_bytes))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (final_state && initial_state && final_state != initial_state &&
+      overlap(final_state, st_bytes, initial_state, st_bytes))
+    return KDA_ERR_INVALID_ARGUMENT;
+  Ws ws;
+  if ((st = carve(workspace, workspace_bytes, T, N, H, ws)) != KDA_OK) return st;
+  if (overlap(workspace, ws.L.total, o, tok * 2) ||
+      overlap(workspace, ws.L.total, final_state, st_bytes))
+    return KDA_ERR_INVALID_ARGUMENT;
+
+  if ((st = run_intra(q, k, v, g, beta, cu_seqlens, T, N, H, scale, ws, stream)) != KDA_OK)
+    return st;
+  RecurArgs ra;
+  ra.blocks = ws.blocks;
+  ra.chunk_first = ws.chunk_first;
+  ra.chunk_info = ws.chunk_info;
+  ra.h0 = initial_state;
+  ra.hT = final_state;
+  ra.o = static_cast<uint16_t *>(o);
+  ra.nc_max = ws.L.nc_max;
+  ra.N = N;
+  ra.H = H;
+  return hip_status(launch_recurrence(ra, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,341 @@
+// Intra-chunk kernel: gate cumsum + strip-GEMMs + (I+L)^-1 + WY factors.
+//
+// One workgroup (4 waves) per (chunk, head).  With G the chunk-local
+// inclusive cumsum of g, Gamma = exp(G), rows i, j of the chunk, and the
+// padding convention q = k = v = 0, g = 0, beta = 0 past a partial chunk's
+// end (so every quantity below is exactly zero or exactly carried there):
+//
+//   Aqk = scale * lower-incl-diag( (Q*Gamma)(K/Gamma)^T )           [64, 64]
+//   L   = strictly-lower( diag(beta) (K*Gamma)(K/Gamma)^T )           [64, 64]
+//   T   = (I + L)^-1,   T' = T diag(beta)
+//   U   = T' V,   W = T' (K*Gamma),   qg = scale Q*Gamma,
+//   kg  = K * exp(G_last - G),   gamma = exp(G_last)
+//
+// KDA TPU report: section 4 (subblock-midpoint strip-GEMMs with bf16 inputs
+// and fp32 accumulation; the fused right-hand side [beta v | beta k 2^G];
+// no row-serial elimination), section 6.1 (cumsum fused in), section 6.2
+// (what the recurrence consumes), section 6.3 (no backward-only columns).
+//
+// Strip-GEMMs.  Aqk and L are built from 16x16 blocks (a, b), a >= b.  Block
+// b's reference row r_b = 16 b + 7 (its midpoint) splits each factor as
+//   exp(G_i - G_j) = exp(G_i - G_{r_b}) * exp(G_{r_b} - G_j),
+// so with g in [-5, 0] each factor stays within 8 * 5 = 40 nats (57.7 bits,
+// well inside the bf16/fp32 exponent range) and rows i past block b only see
+// decay.  Operands are split into hi + lo bf16 and multiplied as
+// hi*hi + hi*lo + lo*hi on v_mfma_f32_16x16x32_bf16.
+//
+// Inverse.  The four diagonal 16x16 blocks use the finite Neumann product
+// (I + X)(I + X^2)(I + X^4)(I + X^8) with X = -L_aa, exact because X is
+// strictly lower (X^16 = 0); the off-diagonal blocks are merged as
+// T_ab = -T_aa sum_{c=b}^{a-1} L_ac T_cb, one block diagonal at a time.  All
+// of it runs in fp32 on v_mfma_f32_16x16x4_f32.
+#include "kda_cumsum.h"
+#include "kda_internal.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int QK_LD = 136;  // bf16 row stride in LDS (128 + 8 pad)
+constexpr int G_LD = 132;   // fp32 row stride (128 + 4 pad)
+constexpr int LT_LD = 68;   // fp32 row stride of the 64 x 64 L and T
+constexpr int Y_LD = 17;    // 16 x 16 scratch row stride
+
+struct __align__(16) IntraSmem {
+  bf16_t q[BT][QK_LD];
+  bf16_t k[BT][QK_LD];
+  bf16_t v[BT][QK_LD];
+  float G[BT][G_LD];
+  float L[BT][LT_LD];
+  float T[BT][LT_LD];
+  float Y[4][16][Y_LD];
+  float beta[BT];
+  float tot[8][DK];
+};
+
+// The six (token tile, token slab) pairs of a 64 x 64 lower-triangular
+// operand that hold any j <= i; index = AQK_IDX(mt, s).
+__device__ constexpr int LT_MT[6] = {0, 1, 2, 2, 3, 3};
+__device__ constexpr int LT_S[6] = {0, 0, 0, 1, 0, 1};
+
+__device__ __forceinline__ void store_bf16x4(uint8_t *p, const bf16x4 &x) {
+  *reinterpret_cast<bf16x4 *>(p) = x;
+}
+__device__ __forceinline__ void store_bf16x8(uint8_t *p, const bf16x8 &x) {
+  *reinterpret_cast<bf16x8 *>(p) = x;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void intra_kernel(IntraArgs a) {
+  __shared__ IntraSmem sm;
+  const int64_t c = blockIdx.x / a.H;
+  const int h = blockIdx.x % a.H;
+  if (c >= a.chunk_first[a.N]) return;
+  const int4 info = a.chunk_info[c];
+  const int64_t t0 = info.x;
+  const int n = info.y;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, nn = l & 15, grp = l >> 4;
+  uint8_t *blk = a.blocks + ((int64_t)h * a.nc_max + c) * BLOCK_BYTES;
+
+  // ---- q, k, v, beta into LDS (zero past the chunk end); G by cumsum ----
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int ci = tid + 256 * it, row = ci >> 4, c16 = ci & 15;
+    uint4 vq = make_uint4(0, 0, 0, 0), vk = vq, vv = vq;
+    if (row < n) {
+      const int64_t off = ((t0 + row) * a.H + h) * DK + c16 * 8;
+      vq = *reinterpret_cast<const uint4 *>(a.q + off);
+      vk = *reinterpret_cast<const uint4 *>(a.k + off);
+      vv = *reinterpret_cast<const uint4 *>(a.v + off);
+    }
+    *reinterpret_cast<uint4 *>(&sm.q[row][c16 * 8]) = vq;
+    *reinterpret_cast<uint4 *>(&sm.k[row][c16 * 8]) = vk;
+    *reinterpret_cast<uint4 *>(&sm.v[row][c16 * 8]) = vv;
+  }
+  if (tid < BT) sm.beta[tid] = tid < n ? a.beta[(t0 + tid) * a.H + h] : 0.f;
+  chunk_gate_cumsum<G_LD>(a.g, t0, n, a.H, h, sm.G, sm.tot);
+  __syncthreads();
+
+  // ---- Aqk^T and L blocks by hi/lo strip-GEMMs ----
+  {
+    constexpr int PA[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+    constexpr int PB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+    for (int p = w; p < 10; p += 4) {
+      const int ba = PA[p], bb = PB[p];
+      const int rref = SB * bb + SB_REF;
+      const int j = SB * bb + nn;  // row of the column-side factor k~
+      const int i = SB * ba + nn;  // row of the row-side factors q~, k^
+      f32x4 accA = zero4(), accL = zero4();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int ch0 = 32 * s + 8 * grp;
+        bf16x8 kth, ktl, qth, qtl, krh, krl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ch = ch0 + e;
+          const float Gr = sm.G[rref][ch], Gj = sm.G[j][ch], Gi = sm.G[i][ch];
+          const float fk = exp_nat(Gr - Gj);
+          const float fq = exp_nat(Gi - Gr);
+          split_bf16((float)sm.k[j][ch] * fk, kth, ktl, e);
+          split_bf16((float)sm.q[i][ch] * fq, qth, qtl, e);
+          split_bf16((float)sm.k[i][ch] * fq, krh, krl, e);
+        }
+        // Aqk^T block: rows j (A = k~), columns i (B = q~)
+        accA = mfma_bf16(kth, qth, accA);
+        accA = mfma_bf16(kth, qtl, accA);
+        accA = mfma_bf16(ktl, qth, accA);
+        // L block: rows i (A = k^), columns j (B = k~)
+        accL = mfma_bf16(krh, kth, accL);
+        accL = mfma_bf16(krh, ktl, accL);
+        accL = mfma_bf16(krl, kth, accL);
+      }
+      // Aqk^T: lane holds [j = 16bb + 4grp + r][i = 16ba + nn]; it becomes half
+      // (bb & 1) of the recurrence's Aqk fragment (mt = ba, s = bb >> 1).
+      bf16x4 ah, al;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool keep = (ba > bb) || (4 * grp + r <= nn);
+        split_bf16(keep ? accA[r] * a.scale : 0.f, ah, al, r);
+      }
+      const int idx = AQK_IDX(ba, bb >> 1), half = bb & 1;
+      store_bf16x4(blk + OFF_AQK + (idx * 64 + l) * 16 + half * 8, ah);
+      store_bf16x4(blk + OFF_AQK + ((AQK_FRAGS + idx) * 64 + l) * 16 + half * 8, al);
+      if (ba == bb && (ba & 1) == 0) {
+        // blocks (0,1) and (2,3) lie above the diagonal: zero half 1
+        const bf16x4 z = {(bf16_t)0.f, (bf16_t)0.f, (bf16_t)0.f, (bf16_t)0.f};
+        store_bf16x4(blk + OFF_AQK + (idx * 64 + l) * 16 + 8, z);
+        store_bf16x4(blk + OFF_AQK + ((AQK_FRAGS + idx) * 64 + l) * 16 + 8, z);
+      }
+      // L: lane holds [i = 16ba + 4grp + r][j = 16bb + nn], row-scaled by beta_i
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int il = 4 * grp + r;
+        const bool keep = (ba > bb) || (nn < il);
+        sm.L[SB * ba + il][SB * bb + nn] = keep ? accL[r] * sm.beta[SB * ba + il] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- diagonal blocks of T: Neumann product, wave w owns block w ----
+  {
+    const int d0 = SB * w;
+    float(*Y)[Y_LD] = sm.Y[w];
+    f32x4 P;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * grp + r;
+      const float x = (nn < m) ? -sm.L[d0 + m][d0 + nn] : 0.f;
+      Y[m][nn] = x;
+      P[r] = (nn == m) ? 1.f : x;
+      sm.T[d0 + m][d0 + nn] = P[r];
+    }
+    __syncthreads();
+    for (int it = 0; it < 3; ++it) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) acc = mfma_f32(Y[nn][4 * s4 + grp], Y[4 * s4 + grp][nn], acc);
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Y[4 * grp + r][nn] = acc[r];
+      __syncthreads();
+      acc = P;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        acc = mfma_f32(sm.T[d0 + nn][d0 + 4 * s4 + grp], Y[4 * s4 + grp][nn], acc);
+      __syncthreads();
+      P = acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.T[d0 + 4 * grp + r][d0 + nn] = acc[r];
+      __syncthreads();
+    }
+  }
+
+  // ---- off-diagonal blocks: T_ab = -T_aa sum_{c=b}^{a-1} L_ac T_cb ----
+  for (int d = 1; d < 4; ++d) {
+    const bool act = w < 4 - d;
+    const int ba = w + d, bb = w;
+    float(*Y)[Y_LD] = sm.Y[w];
+    if (act) {
+      f32x4 acc = zero4();
+      for (int cb = bb; cb < ba; ++cb) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          acc = mfma_f32(sm.L[SB * ba + nn][SB * cb + 4 * s4 + grp],
+                         sm.T[SB * cb + 4 * s4 + grp][SB * bb + nn], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Y[4 * grp + r][nn] = acc[r];
+    }
+    __syncthreads();
+    if (act) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        acc = mfma_f32(sm.T[SB * ba + nn][SB * ba + 4 * s4 + grp], Y[4 * s4 + grp][nn], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.T[SB * ba + 4 * grp + r][SB * bb + nn] = -acc[r];
+    }
+    __syncthreads();
+  }
+
+  // ---- T' = T diag(beta) as hi/lo A fragments (rows i, 8 columns j) ----
+  bf16x8 th[6], tl[6];
+#pragma unroll
+  for (int x = 0; x < 6; ++x) {
+    const int i = SB * LT_MT[x] + nn;
+    const int j0 = 32 * LT_S[x] + 8 * grp;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int jj = j0 + e;
+      const float val = (jj <= i) ? sm.T[i][jj] * sm.beta[jj] : 0.f;
+      split_bf16(val, th[x], tl[x], e);
+    }
+  }
+
+  // ---- U = T' V: wave w writes value tiles nt = 2w, 2w+1 (C layout) ----
+#pragma unroll
+  for (int q2 = 0; q2 < 2; ++q2) {
+    const int nt = 2 * w + q2;
+    const int col = 16 * nt + nn;
+    bf16x8 vb[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vb[s][e] = sm.v[32 * s + 8 * grp + e][col];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s <= (mt >> 1); ++s) {
+        const int x = AQK_IDX(mt, s);
+        acc = mfma_bf16(th[x], vb[s], acc);
+        acc = mfma_bf16(tl[x], vb[s], acc);
+      }
+      bf16x4 u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) u[r] = (bf16_t)acc[r];
+      store_bf16x4(blk + OFF_U + ((nt * 4 + mt) * 64 + l) * 8, u);
+    }
+  }
+
+  // ---- W^T = (K*Gamma)^T T'^T: wave w owns key tiles 2w, 2w+1 ----
+#pragma unroll
+  for (int q2 = 0; q2 < 2; ++q2) {
+    const int mtc = 2 * w + q2;
+    const int ch = 16 * mtc + nn;
+    bf16x8 kh[2], kl[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int jj = 32 * s + 8 * grp + e;
+        split_bf16((float)sm.k[jj][ch] * exp_nat(sm.G[jj][ch]), kh[s], kl[s], e);
+      }
+#pragma unroll
+    for (int nti = 0; nti < 4; ++nti) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s <= (nti >> 1); ++s) {
+        const int x = AQK_IDX(nti, s);
+        acc = mfma_bf16(kh[s], th[x], acc);
+        acc = mfma_bf16(kh[s], tl[x], acc);
+        acc = mfma_bf16(kl[s], th[x], acc);
+      }
+      // lane holds W^T[16 mtc + 4grp + r][16 nti + nn] -> -W, half (mtc & 1)
+      // of the fragment (token tile nti, key slab mtc >> 1)
+      bf16x4 wv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wv[r] = (bf16_t)(-acc[r]);
+      store_bf16x4(blk + OFF_WN + ((nti * 4 + (mtc >> 1)) * 64 + l) * 16 + (mtc & 1) * 8, wv);
+    }
+  }
+
+  // ---- qg = scale q Gamma fragments: wave w owns token tile w ----
+  {
+    const int i = SB * w + nn;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ch = 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3);
+        f[e] = (bf16_t)(a.scale * (float)sm.q[i][ch] * exp_nat(sm.G[i][ch]));
+      }
+      store_bf16x8(blk + OFF_QG + ((w * 4 + s) * 64 + l) * 16, f);
+    }
+  }
+
+  // ---- kg^T fragments: wave w owns key tiles 2w, 2w+1 ----
+#pragma unroll
+  for (int q2 = 0; q2 < 2; ++q2) {
+    const int mtc = 2 * w + q2;
+    const int ch = 16 * mtc + nn;
+    const float Glast = sm.G[BT - 1][ch];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int jj = 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3);
+        f[e] = (bf16_t)((float)sm.k[jj][ch] * exp_nat(Glast - sm.G[jj][ch]));
+      }
+      store_bf16x8(blk + OFF_KGT + ((mtc * 2 + s) * 64 + l) * 16, f);
+    }
+  }
+
+  if (tid < DK) {
+    *reinterpret_cast<float *>(blk + OFF_GAM + tid * 4) = exp_nat(sm.G[BT - 1][tid]);
+  }
+}
+
+hipError_t launch_intra(const IntraArgs &a, hipStream_t stream) {
+  if (a.nc_max <= 0) return hipSuccess;
+  hipLaunchKernelGGL(intra_kernel, dim3((unsigned)(a.nc_max * a.H)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace kda

@@ -1,0 +1,42 @@
+// Host-side launchers, one per kernel; each lives in its kernel's source
+// file and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+hipError_t launch_chunk_table(const int32_t *cu, int64_t T, int32_t N, int64_t nc_max,
+                              int32_t *chunk_first, int4 *chunk_info, int32_t *flags,
+                              hipStream_t stream);
+
+hipError_t launch_gate_cumsum(const float *g, const int32_t *chunk_first, const int4 *chunk_info,
+                              int64_t nc_max, int32_t N, int32_t H, float *G, hipStream_t stream);
+
+struct IntraArgs {
+  const uint16_t *q, *k, *v;  // bf16 bits [T, H, 128]
+  const float *g;             // [T, H, 128]
+  const float *beta;          // [T, H]
+  const int32_t *chunk_first; // [N + 1]
+  const int4 *chunk_info;     // [nc_max]
+  uint8_t *blocks;            // H * nc_max intermediate blocks
+  int64_t nc_max;
+  int32_t N, H;
+  float scale;
+};
+hipError_t launch_intra(const IntraArgs &a, hipStream_t stream);
+
+struct RecurArgs {
+  const uint8_t *blocks;
+  const int32_t *chunk_first;
+  const int4 *chunk_info;
+  const float *h0;      // [N, H, 128, 128] or null
+  float *hT;            // [N, H, 128, 128] or null
+  uint16_t *o;          // bf16 bits [T, H, 128]
+  int64_t nc_max;
+  int32_t N, H;
+};
+hipError_t launch_recurrence(const RecurArgs &a, hipStream_t stream);
+
+}  // namespace kda

@@ -231,3 +231,26 @@ def algorithmic_bytes(w: Workload) -> int:
 def algorithmic_flops(w: Workload) -> int:
     """FLOP of the chunked method (BT=64) per (token, head): 154,624."""
     return int(w.T * w.H * 154624)
+
+
+def to_torch(w: Workload, device="cuda") -> dict:
+    """Device copies of a workload's tensors (bf16 stays bit-identical)."""
+    import torch
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device).view(
+            torch.bfloat16)
+
+    def f32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+    return {"q": bf(w.q), "k": bf(w.k), "v": bf(w.v), "g": f32(w.g), "beta": f32(w.beta),
+            "cu_seqlens": torch.from_numpy(w.cu_seqlens.astype(np.int32)).to(device),
+            "initial_state": None if w.initial_state is None else f32(w.initial_state)}
+
+
+def bf16_tensor_to_f32(t) -> np.ndarray:
+    """A bf16 torch tensor (any device) as exact fp32 numpy values."""
+    import torch
+    return t.detach().to("cpu").view(torch.int16).numpy().view(np.uint16).astype(
+        np.uint32).__lshift__(16).view(np.float32)

@@ -1,0 +1,161 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) KDA chunked-prefill forward library.
+ *
+ * The operation (KDA TPU report, sections 1-2 and 6.2; MI355X serving post,
+ * section 1.1): the Kimi Delta Attention gated delta rule with per-channel
+ * decay, for every packed sequence s and head h,
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * with a [128 (key), 128 (value)] fp32 state per (sequence, head), computed
+ * in 64-token chunks (16-token subblocks inside each chunk).  The gate must
+ * satisfy -5 <= g <= 0 (the bounded gate, lower_bound = -5): the chunk math
+ * relies on it to keep bf16 strip factors within range.
+ *
+ * Conventions for every entry point below:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous
+ *     row-major, and 16-byte aligned (beta and cu_seqlens: 4-byte aligned).
+ *   - The library allocates nothing, never synchronises the device, and only
+ *     enqueues work on `stream` (0 = the null stream).
+ *   - Host-checkable argument errors are reported before anything is
+ *     launched; a launch failure is reported as KDA_ERR_HIP.
+ *   - Device-content contracts are the caller's: cu_seqlens starts at 0,
+ *     never decreases and ends at T; g lies in [-5, 0].  Malformed
+ *     cu_seqlens never make a kernel read or write out of bounds (the chunk
+ *     table clamps it into [0, T]) but the results are then unspecified.
+ *   - No global mutable state: concurrent calls on different streams with
+ *     different workspaces are safe.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, misalignment */
+    KDA_ERR_UNSUPPORTED = 2,        /* sizes beyond what the kernels index      */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 3,
+    KDA_ERR_HIP = 4                 /* a kernel launch failed                   */
+} kda_status;
+
+/* Fixed problem geometry of this library. */
+#define KDA_HEAD_DIM 128   /* K = V = 128                                   */
+#define KDA_CHUNK 64       /* BT: tokens per chunk                           */
+#define KDA_SUBBLOCK 16    /* SB: tokens per subblock                        */
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *kda_status_string(kda_status s);
+
+/*
+ * Bytes of workspace kda_chunk_fwd / kda_chunk_intra need for T packed
+ * tokens, N sequences and H heads.  The bound uses the worst-case chunk
+ * count floor((T + 63 N) / 64), so it depends only on sizes, never on the
+ * contents of cu_seqlens.  Returns 0 for invalid sizes (T < 0, N < 1,
+ * H < 1).
+ */
+size_t kda_chunk_fwd_workspace_size(int64_t T, int32_t N, int32_t H);
+
+/*
+ * Chunked KDA prefill forward (KDA TPU report section 6: gate cumsum and
+ * intra-chunk in one kernel, chunk recurrence and output in another; section
+ * 6.5: a flat grid over the chunks that exist).
+ *
+ *   q, k          bf16 [T, H, 128]; k is expected L2-normalised per token
+ *   v             bf16 [T, H, 128]
+ *   g             fp32 [T, H, 128]   log-decay per key channel, in [-5, 0]
+ *   beta          fp32 [T, H]        write strength
+ *   initial_state fp32 [N, H, 128, 128] (key-major: S[key][value]) or NULL,
+ *                 which means zeros
+ *   cu_seqlens    int32 [N + 1] device array of packed sequence offsets;
+ *                 zero-length sequences are allowed
+ *   T, N, H       tokens, sequences (N >= 1), heads (1 <= H <= 65535);
+ *                 T <= 2^31 - 1 and T * H * 128 must fit in int64
+ *   scale         multiplies S^T q (1/sqrt(128) for the usual scaling)
+ *   o             bf16 [T, H, 128] output, rounded to nearest even; must not
+ *                 alias any input
+ *   final_state   fp32 [N, H, 128, 128] output or NULL (not written); may
+ *                 alias initial_state exactly (in-place update)
+ *   workspace     device scratch of workspace_bytes >=
+ *                 kda_chunk_fwd_workspace_size(T, N, H); its contents on
+ *                 entry do not matter and on return are unspecified
+ *   stream        HIP stream the three kernels are enqueued on, in order
+ *
+ * A sequence's outputs depend only on its own tokens and initial state:
+ * they are bitwise identical whichever offset and neighbours it is packed
+ * with.  Results are deterministic run to run.
+ */
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
+                         const float *g, const float *beta,
+                         const float *initial_state, const int32_t *cu_seqlens,
+                         int64_t T, int32_t N, int32_t H, float scale,
+                         void *o, float *final_state,
+                         void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * Step-level entry points.  They run the first steps of kda_chunk_fwd on
+ * their own so that each step can be checked separately; kda_chunk_fwd does
+ * not call them.
+ */
+
+/*
+ * Chunk table (KDA TPU report, section 6.5 flat packed-chunk grid; section
+ * 6.4 worked example).  Writes, for cu_seqlens clamped into [0, T]:
+ *   chunk_first  int32 [N + 1]: index of each sequence's first chunk, with
+ *                chunk_first[N] = number of chunks NC = sum ceil(L_s / 64);
+ *   chunk_info   int32 [NCmax, 4] with NCmax = floor((T + 63 N) / 64): for
+ *                chunk c < NC (token_start, length, sequence, local_index);
+ *                rows c >= NC are (0, 0, -1, -1);
+ *   flags        int32 [1]: 0, or 1 if cu_seqlens had to be clamped.
+ * Returns KDA_ERR_INVALID_ARGUMENT for null pointers or bad sizes.
+ */
+kda_status kda_chunk_table(const int32_t *cu_seqlens, int64_t T, int32_t N,
+                           int32_t *chunk_first, int32_t *chunk_info,
+                           int32_t *flags, hipStream_t stream);
+
+/*
+ * Chunk-local gate cumsum (KDA TPU report section 6.1): G[t, h, :] is the
+ * inclusive sum of g over the tokens of t's chunk up to and including t,
+ * restarting at every chunk and sequence start.  fp32, same layout as g.
+ * Uses `workspace` (>= kda_chunk_fwd_workspace_size(T, N, H) bytes) for the
+ * chunk table.
+ */
+kda_status kda_gate_cumsum(const float *g, const int32_t *cu_seqlens,
+                           int64_t T, int32_t N, int32_t H, float *G,
+                           void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
+ * Chunk table + intra-chunk kernel only: leaves the per-(head, chunk)
+ * intermediates of the fused recurrence in `workspace` (where: see
+ * kda_workspace_layout).  Same arguments as kda_chunk_fwd.
+ */
+kda_status kda_chunk_intra(const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           const int32_t *cu_seqlens, int64_t T, int32_t N,
+                           int32_t H, float scale, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Where things live inside the workspace, for the step-level tests.
+ * kda_workspace_layout fills out[0..4] = byte offsets of (flags,
+ * chunk_first, chunk_info, first intermediate block) and the block size
+ * in bytes; the block of (head h, chunk c) starts at
+ * out[3] + (h * NCmax + c) * out[4].  Returns KDA_ERR_INVALID_ARGUMENT for
+ * bad sizes.
+ */
+kda_status kda_workspace_layout(int64_t T, int32_t N, int32_t H, int64_t out[5]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -18,6 +18,7 @@ Contents
 ``linear_attention``   g = 0, orthonormal keys, S_0 = 0: causal linear
                    attention o_t = scale sum_{s<=t} beta_s (q_t.k_s) v_s.
 ``chunked_fwd``    the chunk (WY/UT) form in fp64 with BT-token chunks.
+``chunk_terms``    the per-chunk quantities of that form (W, U, Aqk, ...).
 ``chunk_table``    per-chunk (sequence, local chunk, start, length, flags).
 ``strip_exponents``  largest |exponent| the subblock-midpoint strip factors
                    need, in nats.
@@ -219,22 +220,44 @@ def chunk_table(cu_seqlens, bt: int = 64):
     return rows
 
 
+def chunk_terms(Q, K, V, g, beta, scale):
+    """fp64 per-chunk quantities of the chunk form for one (sequence, head)
+    chunk of n rows (KDA TPU report, section 4 for L, the inverse and the
+    fused right-hand side [beta v | beta k 2^G]; section 6.2 for what the
+    recurrence consumes).  With G the inclusive cumsum of g over the chunk
+    and Gam = exp(G):
+
+        L   = strictly-lower( diag(beta) (K*Gam)(K/Gam)^T )
+        Tm  = (I + L)^-1
+        U   = Tm (beta * V);   W = Tm (beta * K * Gam)
+        Aqk = scale lower-incl-diag( (Q*Gam)(K/Gam)^T )
+        qg  = scale Q * Gam;   kg = K * exp(G_{n-1} - G);   gamma = exp(G_{n-1})
+    """
+    Q, K, V, g = (np.asarray(a, dtype=np.float64) for a in (Q, K, V, g))
+    bet = np.asarray(beta, dtype=np.float64)
+    n = Q.shape[0]
+    G = np.cumsum(g, axis=0)
+    Gam = np.exp(G)
+    Kp, Km = K * Gam, K * np.exp(-G)
+    L = np.tril(bet[:, None] * (Kp @ Km.T), -1)
+    Tm = np.linalg.solve(np.eye(n) + L, np.eye(n))
+    return dict(G=G, L=L, T=Tm,
+                U=Tm @ (bet[:, None] * V), W=Tm @ (bet[:, None] * Kp),
+                Aqk=scale * np.tril((Q * Gam) @ Km.T), qg=scale * Q * Gam,
+                kg=K * np.exp(G[-1][None, :] - G), gamma=np.exp(G[-1]))
+
+
 def chunked_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, scale=None,
                 bt: int = 64):
     """The chunk (WY/UT) form of the same recurrence, fp64.
 
     Per sequence, head and chunk of n <= bt rows with entry state h (KDA TPU
-    report, section 4 for the fused right-hand side [beta v | beta k 2^G],
-    section 6.2 for the per-chunk dependencies), with G the chunk-local
-    inclusive cumsum of g and Gam = exp(G):
+    report, section 6.2 for the per-chunk dependencies), using
+    ``chunk_terms``:
 
-        L     = strictly-lower( diag(beta) (K*Gam)(K/Gam)^T )
-        Tm    = (I + L)^-1
-        U     = Tm (beta * V);   W = Tm (beta * K * Gam)
         v_new = U - W h
-        o     = scale (Q*Gam) h + Aqk v_new,
-                Aqk = scale lower-incl-diag( (Q*Gam)(K/Gam)^T )
-        h    <- Diag(Gam_{n-1}) h + (K * Gam_{n-1}/Gam)^T v_new
+        o     = qg h + Aqk v_new
+        h    <- Diag(gamma) h + kg^T v_new
 
     o reads the entry state h, never the updated one (section 6.2).
     """
@@ -253,21 +276,11 @@ def chunked_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, scale=None,
                    widen(initial_state)[s, hh].astype(np.float64).copy())
             for c0 in range(a, b, bt):
                 c1 = min(c0 + bt, b)
-                n = c1 - c0
-                Q, K, V = q[c0:c1, hh], k[c0:c1, hh], v[c0:c1, hh]
-                bet = beta[c0:c1, hh]
-                G = np.cumsum(g[c0:c1, hh], axis=0)
-                Gam = np.exp(G)
-                Kp, Km = K * Gam, K * np.exp(-G)
-                L = np.tril(bet[:, None] * (Kp @ Km.T), -1)
-                Tm = np.linalg.solve(np.eye(n) + L, np.eye(n))
-                U = Tm @ (bet[:, None] * V)
-                W = Tm @ (bet[:, None] * Kp)
-                vnew = U - W @ hst
-                Aqk = scale * np.tril((Q * Gam) @ Km.T)
-                o[c0:c1, hh] = scale * (Q * Gam) @ hst + Aqk @ vnew
-                kg = K * np.exp(G[-1][None, :] - G)
-                hst = np.exp(G[-1])[:, None] * hst + kg.T @ vnew
+                t = chunk_terms(q[c0:c1, hh], k[c0:c1, hh], v[c0:c1, hh],
+                                g[c0:c1, hh], beta[c0:c1, hh], scale)
+                vnew = t["U"] - t["W"] @ hst
+                o[c0:c1, hh] = t["qg"] @ hst + t["Aqk"] @ vnew
+                hst = t["gamma"][:, None] * hst + t["kg"].T @ vnew
             fin[s, hh] = hst
     return o, fin
 

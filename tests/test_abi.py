@@ -1,0 +1,111 @@
+"""Host side of the C ABI (no GPU needed): the library loads, exports every
+function include/kda.h declares, sizes its workspace, and rejects bad
+arguments before launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunked_kda_prefill_amd as kda
+from chunked_kda_prefill_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", src)))
+
+
+def test_header_declarations_are_exported():
+    lib = kda.load_library()
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    assert sorted(names) == sorted(_binding.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = kda.load_library()
+    for code, name in _binding.STATUS_NAMES.items():
+        assert lib.kda_status_string(code).decode() == name
+    assert lib.kda_status_string(99).decode() == "KDA_ERR_UNKNOWN"
+
+
+def test_workspace_size_and_layout():
+    T, N, H = 8192, 4, 16
+    lay = kda.workspace_layout(T, N, H)
+    assert lay["nc_max"] == (T + 63 * N) // 64
+    assert lay["block_bytes"] == 78336
+    for key in ("chunk_first", "chunk_info", "blocks"):
+        assert lay[key] % 256 == 0
+    assert lay["chunk_info"] >= lay["chunk_first"] + 4 * (N + 1)
+    assert lay["blocks"] >= lay["chunk_info"] + 16 * lay["nc_max"]
+    assert kda.workspace_size(T, N, H) == lay["blocks"] + H * lay["nc_max"] * 78336
+    assert kda.workspace_size(0, 1, 1) > 0
+    for bad in [(-1, 1, 1), (10, 0, 1), (10, 1, 0)]:
+        assert kda.workspace_size(*bad) == 0
+    assert kda.workspace_size(2**31, 1, 1) == 0          # beyond int32 tokens
+    assert kda.workspace_size(10, 1, 70000) == 0         # beyond the head limit
+
+
+def _fwd(lib, **over):
+    """Call kda_chunk_fwd with fake, aligned, non-null host addresses: every
+    call here must be rejected by host-side validation before any launch."""
+    A = 1 << 20
+    args = dict(q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, h0=None, cu=6 * A, T=128, N=1,
+                H=2, scale=1.0, o=7 * A, hT=8 * A, ws=9 * A, ws_bytes=0, stream=None)
+    args.update(over)
+    return lib.kda_chunk_fwd(args["q"], args["k"], args["v"], args["g"], args["beta"],
+                             args["h0"], args["cu"], args["T"], args["N"], args["H"],
+                             args["scale"], args["o"], args["hT"], args["ws"],
+                             args["ws_bytes"], args["stream"])
+
+
+def test_invalid_arguments_are_rejected_before_launch():
+    lib = kda.load_library()
+    INV, UNS, WS = 1, 2, 3
+    assert _fwd(lib, q=None) == INV
+    assert _fwd(lib, cu=None) == INV
+    assert _fwd(lib, o=None) == INV
+    assert _fwd(lib, ws=None, ws_bytes=10**9) == INV
+    assert _fwd(lib, T=-1) == INV
+    assert _fwd(lib, N=0) == INV
+    assert _fwd(lib, H=0) == INV
+    assert _fwd(lib, H=70000) == UNS
+    assert _fwd(lib, T=2**31) == UNS
+    assert _fwd(lib, q=(1 << 20) + 8) == INV                 # misaligned
+    assert _fwd(lib, beta=(5 << 20) + 2) == INV
+    assert _fwd(lib, ws=(9 << 20) + 16, ws_bytes=10**9) == INV  # workspace not 256-aligned
+    assert _fwd(lib) == WS                                    # workspace too small
+    need = kda.workspace_size(128, 1, 2)
+    assert _fwd(lib, ws_bytes=need - 1) == WS
+    # o aliasing an input, and overlapping (not identical) state buffers
+    assert _fwd(lib, o=(1 << 20) + 64, ws_bytes=need) == INV
+    assert _fwd(lib, h0=8 << 20, hT=(8 << 20) + 256, ws_bytes=need) == INV
+    # o overlapping the workspace
+    assert _fwd(lib, o=(9 << 20) + 4096, ws_bytes=need) == INV
+
+
+def test_step_entry_points_reject_bad_arguments():
+    lib = kda.load_library()
+    P = 1 << 20
+    assert lib.kda_chunk_table(None, 10, 1, P, P, P, None) == 1
+    assert lib.kda_chunk_table(P, 10, 0, P, P, P, None) == 1
+    assert lib.kda_gate_cumsum(P, P, 10, 1, 1, 2 * P, 4 * P, 0, None) == 3
+    assert lib.kda_gate_cumsum(P, P, 10, 1, 1, P, 4 * P, 10**9, None) == 1  # G aliases g
+    assert lib.kda_chunk_intra(P, P, P, P, P, P, 10, 1, 1, 1.0, None, 10**9, None) == 1
+    out = (ctypes.c_int64 * 5)()
+    assert lib.kda_workspace_layout(-5, 1, 1, out) == 1
+
+
+def test_python_wrapper_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _binding.load_library()

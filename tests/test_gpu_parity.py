@@ -1,0 +1,170 @@
+"""End-to-end parity of kda_chunk_fwd against the fp64 oracle, on every
+named workload and on edge cases, plus the varlen bit-exactness contract:
+a sequence's outputs are bitwise the same alone or packed at any offset, in
+any order; empty sequences copy the state; a NULL initial state equals
+explicit zeros; results are deterministic run to run."""
+
+import numpy as np
+import pytest
+
+from chunked_kda_prefill_amd import workloads as wl
+
+from gpu_util import log, parity, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("scale", [None, 1.0], ids=["scale_rsqrt128", "scale_1"])
+def test_tiny(dev, scale):
+    w = wl.tiny()
+    log(f"[case] tiny scale={scale}")
+    o, f = run_gpu(w, dev, scale=scale)
+    o_ref, f_ref = run_oracle(w, scale=scale)
+    parity(o, f, o_ref, f_ref, f"tiny scale={scale}")
+
+
+EDGE = [1, 8, 15, 16, 17, 63, 64, 65, 130, 210]
+
+
+@pytest.mark.parametrize("pinned", [0.0, 1.0], ids=["random_g", "g_at_lower_bound"])
+def test_edge_lengths(dev, pinned):
+    w = wl.small(EDGE, H=2, seed=41, pinned_fraction=pinned, scale=1.0)
+    log(f"[case] edge lengths pinned={pinned}")
+    o, f = run_gpu(w, dev)
+    o_ref, f_ref = run_oracle(w)
+    parity(o, f, o_ref, f_ref, f"edge pinned={pinned}")
+
+
+def test_heads_1_and_8(dev):
+    for H in (1, 8):
+        w = wl.small([100, 64, 3], H=H, seed=42)
+        log(f"[case] H={H}")
+        o, f = run_gpu(w, dev)
+        parity(o, f, *run_oracle(w), f"H={H}")
+
+
+def test_headline(dev):
+    w = wl.headline()
+    log("[case] headline 4x2048 H=16")
+    o, f = run_gpu(w, dev)
+    parity(o, f, *run_oracle(w), "headline")
+
+
+@pytest.mark.parametrize("B", [1, 8, 64])
+def test_batch(dev, B):
+    w = wl.batch(B)
+    heads = [0, 7, 15]
+    log(f"[case] batch B={B} (oracle on heads {heads})")
+    o, f = run_gpu(w, dev)
+    o_ref, f_ref = run_oracle(w, heads=heads)
+    parity(o[:, heads], f[:, heads], o_ref, f_ref, f"batch{B}")
+
+
+def test_sharegpt_like(dev):
+    w = wl.sharegpt_like()
+    heads = [3, 12]
+    log(f"[case] sharegpt-like T={w.T} chunks={w.num_chunks()} (oracle on heads {heads})")
+    o, f = run_gpu(w, dev)
+    o_ref, f_ref = run_oracle(w, heads=heads)
+    parity(o[:, heads], f[:, heads], o_ref, f_ref, "sharegpt_like")
+
+
+def test_long_single_sequence(dev):
+    w = wl.long_single()
+    heads = [0, 47, 95]
+    log(f"[case] long T=16384 H=96 (oracle on heads {heads})")
+    o, f = run_gpu(w, dev)
+    o_ref, f_ref = run_oracle(w, heads=heads)
+    parity(o[:, heads], f[:, heads], o_ref, f_ref, "long")
+
+
+# ---------------------------------------------------------------------------
+# varlen bit-exactness
+# ---------------------------------------------------------------------------
+def _sub(w, order):
+    """Repack a workload with its sequences in `order` (a permutation or a
+    subset), as a new Workload with the same per-sequence data."""
+    cu = w.cu_seqlens
+    idx = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in order]).astype(np.int64)
+    lens = [int(cu[s + 1] - cu[s]) for s in order]
+    ncu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    h0 = None if w.initial_state is None else np.ascontiguousarray(w.initial_state[list(order)])
+    return wl.Workload(name=w.name + "_sub", seed=w.seed, q=w.q[idx], k=w.k[idx], v=w.v[idx],
+                       g=w.g[idx], beta=w.beta[idx], initial_state=h0, cu_seqlens=ncu,
+                       scale=w.scale)
+
+
+def test_varlen_bit_exact(dev):
+    w = wl.small([130, 0, 64, 17, 200, 1, 0, 95], H=3, seed=43)
+    log("[case] varlen bit-exact")
+    o, f = run_gpu(w, dev)
+    cu = w.cu_seqlens
+    # each sequence alone
+    for s in range(w.N):
+        ws = _sub(w, [s])
+        os_, fs = run_gpu(ws, dev)
+        assert np.array_equal(os_, o[cu[s]:cu[s + 1]]), s
+        assert np.array_equal(fs[0], f[s]), s
+    # permuted packing order
+    perm = [4, 7, 0, 3, 1, 6, 2, 5]
+    wp = _sub(w, perm)
+    op, fp = run_gpu(wp, dev)
+    for new, s in enumerate(perm):
+        a, b = wp.cu_seqlens[new], wp.cu_seqlens[new + 1]
+        assert np.array_equal(op[a:b], o[cu[s]:cu[s + 1]])
+        assert np.array_equal(fp[new], f[s])
+    # empty sequences: final = initial, bitwise
+    for s in (1, 6):
+        assert np.array_equal(f[s], w.initial_state[s].astype(np.float64))
+    # run-to-run determinism
+    o2, f2 = run_gpu(w, dev)
+    assert np.array_equal(o, o2) and np.array_equal(f, f2)
+
+
+def test_null_initial_state_equals_zeros(dev):
+    w = wl.small([100, 37], H=2, seed=44, h0="zeros")
+    log("[case] NULL initial_state vs zeros")
+    oz, fz = run_gpu(w, dev)
+    on, fn = run_gpu(w, dev, with_h0=False)
+    assert np.array_equal(oz, on) and np.array_equal(fz, fn)
+
+
+def test_in_place_state_update(dev):
+    import torch
+    import chunked_kda_prefill_amd as kda
+    w = wl.small([90, 64], H=2, seed=45)
+    log("[case] final_state aliasing initial_state")
+    o_ref, f_ref = run_gpu(w, dev)
+    t = wl.to_torch(w, dev)
+    st = t["initial_state"].clone()
+    o, f = kda.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
+                         initial_state=st, final_state=st, scale=w.scale)
+    torch.cuda.synchronize()
+    assert f.data_ptr() == st.data_ptr()
+    assert np.array_equal(st.cpu().numpy().astype(np.float64), f_ref)
+    assert np.array_equal(wl.bf16_tensor_to_f32(o).astype(np.float64), o_ref)
+
+
+def test_split_equals_chain(dev):
+    # running [A; B] equals running A, then B from A's final state (up to the
+    # fp32 hand-over of the state, which the single call never rounds)
+    w = wl.small([300], H=2, seed=46)
+    log("[case] split = chain")
+    o, f = run_gpu(w, dev)
+    cut = 128                                  # a chunk boundary: same chunking
+    wa = wl.Workload(name="a", seed=0, q=w.q[:cut], k=w.k[:cut], v=w.v[:cut], g=w.g[:cut],
+                     beta=w.beta[:cut], initial_state=w.initial_state,
+                     cu_seqlens=np.array([0, cut], np.int32), scale=w.scale)
+    oa, fa = run_gpu(wa, dev)
+    wb = wl.Workload(name="b", seed=0, q=w.q[cut:], k=w.k[cut:], v=w.v[cut:], g=w.g[cut:],
+                     beta=w.beta[cut:], initial_state=fa.astype(np.float32),
+                     cu_seqlens=np.array([0, 300 - cut], np.int32), scale=w.scale)
+    ob, fb = run_gpu(wb, dev)
+    assert np.array_equal(oa, o[:cut])
+    assert np.array_equal(ob, o[cut:]) and np.array_equal(fb, f)
