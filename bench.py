@@ -1,0 +1,205 @@
+#!/usr/bin/env python
+"""KDA chunked-prefill forward benchmark (one MI355X).
+
+A step is one pass of the whole hot path over one packed varlen batch:
+chunk table -> gate cumsum + intra-chunk kernel -> recurrence + output
+kernel.  It is issued as kda_chunk_intra followed by kda_chunk_recurrence
+(the same kernels kda_chunk_fwd enqueues; the bench checks the two paths
+agree bitwise), with HIP events on the launch stream between them so each
+kernel's duration is measured inside the timed region.
+
+Inputs are resident in HBM before timing starts.  Several device copies of
+the inputs are rotated so that every step reads inputs that are not left in
+the 256 MB Infinity Cache by the previous step.
+
+Prints ONE JSON line.  ``--gpus`` above 1 exits: this build runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s at T=8192,H=16,K=V=128 bf16; % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, TFLOP/s
+MALL_BYTES = 256 * 2**20
+BLOCK_BYTES = 78336              # one (head, chunk) intermediate block
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="headline",
+                    help="headline | tiny | batchB | sharegpt | long")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input copies to rotate (0: enough to exceed 2x the MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8,
+                    help="heads of the workload the oracle baseline runs")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run a plain device copy of this size first (counter scale)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {max(args.gpus, world)}); "
+              "the KDA prefill path shards by heads or sequences with no exchange, "
+              "see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import chunked_kda_prefill_amd as kda
+    from chunked_kda_prefill_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.by_name(args.workload)
+    T, N, H = w.T, w.N, w.H
+    nc = w.num_chunks()
+
+    if args.copy_calibration_mib > 0:
+        nb = args.copy_calibration_mib * 2**20
+        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    base = wl.to_torch(w, dev)
+    in_bytes = sum(base[k].numel() * base[k].element_size()
+                   for k in ("q", "k", "v", "g", "beta"))
+    R = args.rotate if args.rotate > 0 else max(1, math.ceil(2 * MALL_BYTES / in_bytes) + 1)
+    sets = [base] + [{k: (None if t is None else t.clone()) for k, t in base.items()}
+                     for _ in range(R - 1)]
+    o = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((N, H, 128, 128), dtype=torch.float32, device=dev)
+    ws = kda.new_workspace(T, N, H, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(s):
+        kda.chunk_intra(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu_seqlens"],
+                        scale=w.scale, workspace=ws)
+        kda.chunk_recurrence(ws, T, N, H, initial_state=s["initial_state"], o=o,
+                             final_state=fin)
+
+    # the two-call step and the single kda_chunk_fwd call agree bitwise
+    step(sets[0])
+    o_ref, f_ref = kda.chunk_fwd(**{k: v for k, v in sets[0].items()}, scale=w.scale)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o.view(torch.int16), o_ref.view(torch.int16)) and
+                torch.equal(fin, f_ref))
+    if not same:
+        raise SystemExit("bench.py: kda_chunk_fwd and intra+recurrence disagree")
+    o_check = o.clone()
+    f_check = fin.clone()
+    del o_ref, f_ref
+
+    for i in range(args.warmup):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s = sets[i % R]
+        ev[i][0].record(stream)
+        kda.chunk_intra(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu_seqlens"],
+                        scale=w.scale, workspace=ws)
+        ev[i][1].record(stream)
+        kda.chunk_recurrence(ws, T, N, H, initial_state=s["initial_state"], o=o,
+                             final_state=fin)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    intra_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    rec_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    intra_us = 1e3 * float(np.mean(intra_ms))
+    rec_us = 1e3 * float(np.mean(rec_ms))
+
+    # --- algorithmic bytes / flops ---------------------------------------
+    path_bytes = wl.algorithmic_bytes(w)
+    path_flops = wl.algorithmic_flops(w)
+    blocks = nc * H
+    h0_bytes = 0 if w.initial_state is None else N * H * 128 * 128 * 4
+    # the intra kernel must read q, k, v, g, beta and write its blocks; the
+    # recurrence must read the blocks (+ initial state) and write o and the
+    # final state
+    intra_bytes = T * H * (3 * 256 + 512 + 4) + blocks * BLOCK_BYTES
+    rec_bytes = blocks * BLOCK_BYTES + h0_bytes + T * H * 256 + N * H * 128 * 128 * 4
+    kern = {"kda_intra": (intra_us, intra_bytes), "kda_recurrence": (rec_us, rec_bytes)}
+    dom = max(kern, key=lambda k: kern[k][0])
+    dom_us, dom_bytes = kern[dom]
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    step_s = elapsed / args.steps
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None,
+                "kernel_us": {"kda_intra(+chunk_table)": round(intra_us, 2),
+                              "kda_recurrence": round(rec_us, 2)},
+                "kernel_bytes_per_launch": {"kda_intra": intra_bytes,
+                                            "kda_recurrence": rec_bytes}}
+    path = {"algorithmic_bytes": path_bytes, "algorithmic_flops": path_flops,
+            "GB/s": round(path_bytes / step_s / 1e9, 1),
+            "hbm_frac": round(path_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+            "TFLOP/s": round(path_flops / step_s / 1e12, 2),
+            "mfma_frac": round(path_flops / step_s / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+    # --- CPU baseline: the fp64 oracle on a bounded sample -----------------
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        hsel = list(range(min(args.cpu_heads, H)))
+        threads = oracle.max_threads()
+        c0 = time.perf_counter()
+        o_or, f_or = oracle.kda_fwd(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, w.initial_state,
+                                    scale=w.scale, heads=hsel)
+        c1 = time.perf_counter()
+        frac = len(hsel) / H
+        cpu = {"value": round(T * frac / (c1 - c0), 1), "unit": "tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{w.name}: all {T} tokens, heads 0..{len(hsel) - 1} of {H} "
+                         f"({c1 - c0:.2f} s wall); tokens/s scaled to all heads"}
+        og = wl.bf16_tensor_to_f32(o_check[:, hsel]).astype(np.float64)
+        fg = f_check[:, hsel].cpu().numpy().astype(np.float64)
+        parity = {"heads_checked": len(hsel),
+                  "o_maxabs": oracle.max_abs_err(og, o_or), "o_relF": oracle.rel_fro_err(og, o_or),
+                  "final_maxabs": oracle.max_abs_err(fg, f_or),
+                  "final_relF": oracle.rel_fro_err(fg, f_or)}
+        parity = {k: (float(f"{v:.3e}") if isinstance(v, float) else v) for k, v in parity.items()}
+
+    out = {
+        "metric": METRIC, "value": round(T / step_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": T, "N": N, "H": H, "K": 128, "V": 128, "BT": 64,
+                   "SB": 16, "chunks": nc, "initial_state": w.initial_state is not None,
+                   "input_copies_rotated": R},
+        "roofline": roofline, "path": path, "cpu_baseline": cpu, "parity_vs_oracle": parity,
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     chunk_fwd,
     chunk_intra,
+    chunk_recurrence,
     chunk_table,
     gate_cumsum,
     load_library,

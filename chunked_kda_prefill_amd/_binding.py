@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPOR
 # Every symbol include/kda.h declares.
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
             "kda_chunk_table", "kda_gate_cumsum", "kda_chunk_intra",
-            "kda_workspace_layout")
+            "kda_workspace_layout", "kda_chunk_recurrence")
 
 
 class KDAError(RuntimeError):
@@ -61,6 +61,8 @@ def load_library():
     lib.kda_gate_cumsum.restype = ctypes.c_int
     lib.kda_chunk_intra.argtypes = [P, P, P, P, P, P, I64, I32, I32, F32, P, SZ, P]
     lib.kda_chunk_intra.restype = ctypes.c_int
+    lib.kda_chunk_recurrence.argtypes = [P, I64, I32, I32, P, P, P, SZ, P]
+    lib.kda_chunk_recurrence.restype = ctypes.c_int
     lib.kda_workspace_layout.argtypes = [I64, I32, I32, ctypes.POINTER(ctypes.c_int64)]
     lib.kda_workspace_layout.restype = ctypes.c_int
     _lib = lib
@@ -221,3 +223,22 @@ def chunk_intra(q, k, v, g, beta, cu_seqlens, scale: Optional[float] = None, wor
         float(scale), _ptr(workspace), workspace.numel(), _stream(q.device))
     _check("kda_chunk_intra", st)
     return workspace
+
+
+def chunk_recurrence(workspace, T: int, N: int, H: int, initial_state=None, o=None,
+                     final_state=None, output_final_state: bool = True, device=None):
+    """Recurrence + output (kda_chunk_recurrence) on a workspace that
+    chunk_intra has just filled; returns (o, final_state)."""
+    torch = _torch()
+    dev = workspace.device if device is None else device
+    if o is None:
+        o = torch.empty((T, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, HEAD_DIM, HEAD_DIM), dtype=torch.float32, device=dev)
+    if initial_state is not None:
+        _expect(initial_state, "initial_state", torch.float32, (N, H, HEAD_DIM, HEAD_DIM))
+    st = load_library().kda_chunk_recurrence(
+        _ptr(initial_state), T, N, H, _ptr(o), _ptr(final_state), _ptr(workspace),
+        workspace.numel(), _stream(dev))
+    _check("kda_chunk_recurrence", st)
+    return o, final_state

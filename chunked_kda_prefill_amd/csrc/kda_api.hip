@@ -129,6 +129,38 @@ kda_status kda_gate_cumsum(const float *g, const int32_t *cu_seqlens, int64_t T,
       launch_gate_cumsum(g, ws.chunk_first, ws.chunk_info, ws.L.nc_max, N, H, G, stream));
 }
 
+static kda_status check_outputs(const float *initial_state, int64_t T, int32_t N, int32_t H,
+                                const void *o, const float *final_state) {
+  if (T > 0 && (!o || !aligned(o, 16))) return KDA_ERR_INVALID_ARGUMENT;
+  if ((initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
+    return KDA_ERR_INVALID_ARGUMENT;
+  const int64_t st_bytes = (int64_t)N * H * DK * DV * 4;
+  if (overlap(o, T * H * DK * 2, final_state, st_bytes) ||
+      overlap(o, T * H * DK * 2, initial_state, st_bytes))
+    return KDA_ERR_INVALID_ARGUMENT;
+  // final_state may alias initial_state exactly, but not partially
+  if (final_state && initial_state && final_state != initial_state &&
+      overlap(final_state, st_bytes, initial_state, st_bytes))
+    return KDA_ERR_INVALID_ARGUMENT;
+  return KDA_OK;
+}
+
+static kda_status run_recurrence(const float *initial_state, int64_t T, int32_t N, int32_t H,
+                                 void *o, float *final_state, const Ws &ws, hipStream_t stream) {
+  RecurArgs ra;
+  ra.blocks = ws.blocks;
+  ra.chunk_first = ws.chunk_first;
+  ra.chunk_info = ws.chunk_info;
+  ra.h0 = initial_state;
+  ra.hT = final_state;
+  ra.o = static_cast<uint16_t *>(o);
+  ra.nc_max = ws.L.nc_max;
+  ra.T = T;
+  ra.N = N;
+  ra.H = H;
+  return hip_status(launch_recurrence(ra, stream));
+}
+
 static kda_status run_intra(const void *q, const void *k, const void *v, const float *g,
                             const float *beta, const int32_t *cu_seqlens, int64_t T, int32_t N,
                             int32_t H, float scale, const Ws &ws, hipStream_t stream) {
@@ -145,6 +177,7 @@ static kda_status run_intra(const void *q, const void *k, const void *v, const f
   ia.chunk_info = ws.chunk_info;
   ia.blocks = ws.blocks;
   ia.nc_max = ws.L.nc_max;
+  ia.T = T;
   ia.N = N;
   ia.H = H;
   ia.scale = scale;
@@ -171,19 +204,13 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
   kda_status st = check_sizes(T, N, H);
   if (st != KDA_OK) return st;
   if ((st = check_inputs(q, k, v, g, beta, cu_seqlens, T)) != KDA_OK) return st;
-  if (T > 0 && (!o || !aligned(o, 16))) return KDA_ERR_INVALID_ARGUMENT;
-  if ((initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
-    return KDA_ERR_INVALID_ARGUMENT;
+  if ((st = check_outputs(initial_state, T, N, H, o, final_state)) != KDA_OK) return st;
   const int64_t tok = T * H * DK;
   const int64_t st_bytes = (int64_t)N * H * DK * DV * 4;
-  // o must not alias any input; final_state may only alias initial_state exactly
+  // o must not alias any input
   if (overlap(o, tok * 2, q, tok * 2) || overlap(o, tok * 2, k, tok * 2) ||
       overlap(o, tok * 2, v, tok * 2) || overlap(o, tok * 2, g, tok * 4) ||
-      overlap(o, tok * 2, beta, T * H * 4) || overlap(o, tok * 2, final_state, st_bytes) ||
-      overlap(o, tok * 2, initial_state, st_bytes))
-    return KDA_ERR_INVALID_ARGUMENT;
-  if (final_state && initial_state && final_state != initial_state &&
-      overlap(final_state, st_bytes, initial_state, st_bytes))
+      overlap(o, tok * 2, beta, T * H * 4))
     return KDA_ERR_INVALID_ARGUMENT;
   Ws ws;
   if ((st = carve(workspace, workspace_bytes, T, N, H, ws)) != KDA_OK) return st;
@@ -193,17 +220,22 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
 
   if ((st = run_intra(q, k, v, g, beta, cu_seqlens, T, N, H, scale, ws, stream)) != KDA_OK)
     return st;
-  RecurArgs ra;
-  ra.blocks = ws.blocks;
-  ra.chunk_first = ws.chunk_first;
-  ra.chunk_info = ws.chunk_info;
-  ra.h0 = initial_state;
-  ra.hT = final_state;
-  ra.o = static_cast<uint16_t *>(o);
-  ra.nc_max = ws.L.nc_max;
-  ra.N = N;
-  ra.H = H;
-  return hip_status(launch_recurrence(ra, stream));
+  return run_recurrence(initial_state, T, N, H, o, final_state, ws, stream);
+}
+
+kda_status kda_chunk_recurrence(const float *initial_state, int64_t T, int32_t N, int32_t H,
+                                void *o, float *final_state, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  kda_status st = check_sizes(T, N, H);
+  if (st != KDA_OK) return st;
+  if ((st = check_outputs(initial_state, T, N, H, o, final_state)) != KDA_OK) return st;
+  Ws ws;
+  if ((st = carve(workspace, workspace_bytes, T, N, H, ws)) != KDA_OK) return st;
+  if (overlap(workspace, ws.L.total, o, T * H * DK * 2) ||
+      overlap(workspace, ws.L.total, final_state, (int64_t)N * H * DK * DV * 4) ||
+      overlap(workspace, ws.L.total, initial_state, (int64_t)N * H * DK * DV * 4))
+    return KDA_ERR_INVALID_ARGUMENT;
+  return run_recurrence(initial_state, T, N, H, o, final_state, ws, stream);
 }
 
 }  // extern "C"

@@ -74,8 +74,10 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraArgs a) {
   const int h = blockIdx.x % a.H;
   if (c >= a.chunk_first[a.N]) return;
   const int4 info = a.chunk_info[c];
-  const int64_t t0 = info.x;
-  const int n = info.y;
+  // the chunk table is written by the same call; clamping keeps even a
+  // corrupted one in bounds
+  const int64_t t0 = info.x < 0 ? 0 : (info.x > a.T ? a.T : info.x);
+  const int n = (int)(info.y < 0 ? 0 : (info.y > a.T - t0 ? a.T - t0 : (info.y > BT ? BT : info.y)));
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, nn = l & 15, grp = l >> 4;
   uint8_t *blk = a.blocks + ((int64_t)h * a.nc_max + c) * BLOCK_BYTES;

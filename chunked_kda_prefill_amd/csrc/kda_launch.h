@@ -21,7 +21,7 @@ struct IntraArgs {
   const int32_t *chunk_first; // [N + 1]
   const int4 *chunk_info;     // [nc_max]
   uint8_t *blocks;            // H * nc_max intermediate blocks
-  int64_t nc_max;
+  int64_t nc_max, T;
   int32_t N, H;
   float scale;
 };
@@ -34,7 +34,7 @@ struct RecurArgs {
   const float *h0;      // [N, H, 128, 128] or null
   float *hT;            // [N, H, 128, 128] or null
   uint16_t *o;          // bf16 bits [T, H, 128]
-  int64_t nc_max;
+  int64_t nc_max, T;
   int32_t N, H;
 };
 hipError_t launch_recurrence(const RecurArgs &a, hipStream_t stream);

@@ -39,7 +39,12 @@ __global__ __launch_bounds__(64) void recurrence_kernel(RecurArgs a) {
   if (chain >= (int64_t)a.N * a.H) return;
   const int s = (int)(chain / a.H), h = (int)(chain % a.H);
   const int l = threadIdx.x, nn = l & 15, grp = l >> 4;
-  const int c_beg = a.chunk_first[s], c_end = a.chunk_first[s + 1];
+  // chunk range and token ranges are clamped so that a workspace that does
+  // not hold a valid chunk table can never send this kernel out of bounds
+  const int64_t nc_max = a.nc_max;
+  int64_t c_beg = a.chunk_first[s], c_end = a.chunk_first[s + 1];
+  c_beg = c_beg < 0 ? 0 : (c_beg > nc_max ? nc_max : c_beg);
+  c_end = c_end < c_beg ? c_beg : (c_end > nc_max ? nc_max : c_end);
   const int64_t st_base = ((int64_t)s * a.H + h) * DK * DV;
 
   // state slice: key tiles t = 0..7, value tiles 2*quarter + q2
@@ -55,10 +60,10 @@ __global__ __launch_bounds__(64) void recurrence_kernel(RecurArgs a) {
         S[t][q2][r] = a.h0 ? a.h0[st_base + row * DV + col] : 0.f;
       }
 
-  for (int c = c_beg; c < c_end; ++c) {
+  for (int64_t c = c_beg; c < c_end; ++c) {
     const int4 info = a.chunk_info[c];
-    const int64_t t0 = info.x;
-    const int n = info.y;
+    const int64_t t0 = info.x < 0 ? 0 : (info.x > a.T ? a.T : info.x);
+    const int n = (int)(info.y < 0 ? 0 : (info.y > a.T - t0 ? a.T - t0 : info.y));
     const uint8_t *blk = a.blocks + ((int64_t)h * a.nc_max + c) * BLOCK_BYTES;
 
     // entry state as bf16 B operands (k slabs of 32 key rows)

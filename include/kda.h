@@ -83,9 +83,10 @@ size_t kda_chunk_fwd_workspace_size(int64_t T, int32_t N, int32_t H);
  *                 alias any input
  *   final_state   fp32 [N, H, 128, 128] output or NULL (not written); may
  *                 alias initial_state exactly (in-place update)
- *   workspace     device scratch of workspace_bytes >=
+ *   workspace     256-byte aligned device scratch of workspace_bytes >=
  *                 kda_chunk_fwd_workspace_size(T, N, H); its contents on
- *                 entry do not matter and on return are unspecified
+ *                 entry do not matter and on return are unspecified; it
+ *                 must not overlap o or final_state
  *   stream        HIP stream the three kernels are enqueued on, in order
  *
  * A sequence's outputs depend only on its own tokens and initial state:
@@ -101,9 +102,9 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
                          hipStream_t stream);
 
 /*
- * Step-level entry points.  They run the first steps of kda_chunk_fwd on
- * their own so that each step can be checked separately; kda_chunk_fwd does
- * not call them.
+ * Step-level entry points.  They run the steps of kda_chunk_fwd on their
+ * own so that each step can be checked and timed separately; kda_chunk_fwd
+ * does not call them.
  */
 
 /*
@@ -143,6 +144,21 @@ kda_status kda_chunk_intra(const void *q, const void *k, const void *v,
                            const int32_t *cu_seqlens, int64_t T, int32_t N,
                            int32_t H, float scale, void *workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Chunk recurrence + output only (KDA TPU report section 6.2: the state
+ * stays on chip across a sequence's chunks and the output is formed in the
+ * same pass): runs the second half of kda_chunk_fwd on a workspace that
+ * kda_chunk_intra has just filled for the same T, N, H and inputs, on the
+ * same stream.  kda_chunk_intra followed by kda_chunk_recurrence computes
+ * exactly what kda_chunk_fwd computes.  Arguments as in kda_chunk_fwd; the
+ * workspace must not overlap o or either state buffer.  A workspace that
+ * kda_chunk_intra did not fill gives unspecified results, never an
+ * out-of-bounds access.
+ */
+kda_status kda_chunk_recurrence(const float *initial_state, int64_t T, int32_t N, int32_t H,
+                                void *o, float *final_state, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Where things live inside the workspace, for the step-level tests.

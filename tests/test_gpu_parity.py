@@ -168,3 +168,19 @@ def test_split_equals_chain(dev):
     ob, fb = run_gpu(wb, dev)
     assert np.array_equal(oa, o[:cut])
     assert np.array_equal(ob, o[cut:]) and np.array_equal(fb, f)
+
+
+def test_intra_then_recurrence_equals_fwd(dev):
+    import torch
+    import chunked_kda_prefill_amd as kda
+    w = wl.small([150, 64, 3, 0, 77], H=3, seed=47)
+    log("[case] intra + recurrence == fwd (bitwise)")
+    t = wl.to_torch(w, dev)
+    o1, f1 = kda.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
+                           initial_state=t["initial_state"], scale=w.scale)
+    ws = kda.chunk_intra(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
+                         scale=w.scale)
+    o2, f2 = kda.chunk_recurrence(ws, w.T, w.N, w.H, initial_state=t["initial_state"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(f1, f2)

@@ -121,11 +121,16 @@ def test_intra_intermediates(dev, lens, scale):
                 worst[name] = max(worst.get(name, 0.0), e)
                 # rows past a partial chunk's end are exactly zero
                 assert not np.any(x[n:]), (name, c, h)
-            eg = oracle.rel_fro_err(got["gamma"], ref["gamma"])
+            # gamma = exp(G_last) underflows fp32 for long strong decays:
+            # absolute error everywhere, relative where it is representable
+            ga, gr = got["gamma"], ref["gamma"]
+            big = gr > 1e-30
+            eg = max(float(np.max(np.abs(ga - gr))),
+                     float(np.max(np.abs(ga[big] / gr[big] - 1.0))) if big.any() else 0.0)
             worst["gamma"] = max(worst.get("gamma", 0.0), eg)
     log("[intra] worst relF " + " ".join(f"{k}={v:.2e}" for k, v in worst.items()))
     # bf16 storage of one rounding: ~2^-9 relative per element
     for name in ("W", "U", "qg", "kg"):
         assert worst[name] < 4e-3, (name, worst[name])
     assert worst["Aqk"] < 1e-4          # stored as hi + lo bf16
-    assert worst["gamma"] < 1e-5
+    assert worst["gamma"] < 1e-4
