@@ -24,6 +24,9 @@ HIPCC_FLAGS = [
     "-shared",
     # keep the compiler from emitting packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in arch VGPRs: the recurrence rescales and converts
+    # its state every chunk, which costs AGPR<->VGPR moves otherwise
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -1,7 +1,7 @@
 // C ABI of libkda: argument validation on the host, then kernel launches on
 // the caller's stream.  Nothing here reads device memory, allocates, or
 // synchronises.
-#include "../../include/kda.h"
+#include "kda.h"
 #include "kda_internal.h"
 #include "kda_launch.h"
 
@@ -25,9 +25,9 @@ kda_status check_sizes(int64_t T, int32_t N, int32_t H) {
   if (T < 0 || N < 1 || H < 1) return KDA_ERR_INVALID_ARGUMENT;
   if (T > INT32_MAX || H > 65535) return KDA_ERR_UNSUPPORTED;
   const int64_t nc_max = nc_max_of(T, N);
-  // grids are 1-D: (chunk slots x heads) and (chains / 8 x 32) workgroups
+  // grids are 1-D: (chunk slots x heads) and (sequences x heads) workgroups
   if (nc_max * (int64_t)H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
-  if (((int64_t)N * H + 7) / 8 * 32 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if ((int64_t)N * H > INT32_MAX) return KDA_ERR_UNSUPPORTED;
   return KDA_OK;
 }
 

@@ -82,27 +82,29 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t *__restr
   if (tid == 0) flags[0] = bad_s;
 }
 
-// Standalone chunk-local cumsum: one workgroup per (chunk slot, head).
+// Standalone chunk-local cumsum: one workgroup per (chunk slot, head), with
+// the intra-chunk kernel's thread count so the summation order is the same.
 constexpr int CS_GLD = 132;
 
-__global__ __launch_bounds__(256) void gate_cumsum_kernel(const float *__restrict__ g,
+__global__ __launch_bounds__(INTRA_THREADS) void gate_cumsum_kernel(const float *__restrict__ g,
                                                           const int32_t *__restrict__ chunk_first,
                                                           const int4 *__restrict__ chunk_info,
                                                           int32_t N, int32_t H,
                                                           float *__restrict__ Gout) {
-  __shared__ float G[BT][CS_GLD];
-  __shared__ float tot[8][DK];
+  __shared__ __align__(16) float G[BT][CS_GLD];
+  __shared__ __align__(16) float tot[INTRA_THREADS / 32][DK];
   const int64_t c = blockIdx.x / H;
   const int h = blockIdx.x % H;
   if (c >= chunk_first[N]) return;
   const int4 info = chunk_info[c];
   const int64_t t0 = info.x;
   const int n = info.y;
-  chunk_gate_cumsum<CS_GLD>(g, t0, n, H, h, G, tot);
+  chunk_gate_cumsum<INTRA_THREADS>(g, t0, n, H, h, &G[0][0],
+                         [](int row, int ch) { return row * CS_GLD + ch; }, &tot[0][0]);
   __syncthreads();
   // write back rows < n: 32 lanes per row, 16 bytes each
   const int tid = threadIdx.x;
-  for (int idx = tid; idx < BT * 32; idx += 256) {
+  for (int idx = tid; idx < BT * 32; idx += INTRA_THREADS) {
     const int i = idx >> 5, c4 = idx & 31;
     if (i < n) {
       *reinterpret_cast<float4 *>(Gout + ((t0 + i) * (int64_t)H + h) * DK + c4 * 4) =
@@ -122,7 +124,8 @@ hipError_t launch_chunk_table(const int32_t *cu, int64_t T, int32_t N, int64_t n
 hipError_t launch_gate_cumsum(const float *g, const int32_t *chunk_first, const int4 *chunk_info,
                               int64_t nc_max, int32_t N, int32_t H, float *G, hipStream_t stream) {
   if (nc_max <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gate_cumsum_kernel, dim3((unsigned)(nc_max * H)), dim3(256), 0, stream, g,
+  hipLaunchKernelGGL(gate_cumsum_kernel, dim3((unsigned)(nc_max * H)), dim3(INTRA_THREADS), 0,
+                     stream, g,
                      chunk_first, chunk_info, N, H, G);
   return hipGetLastError();
 }

@@ -1,6 +1,6 @@
 // Intra-chunk kernel: gate cumsum + strip-GEMMs + (I+L)^-1 + WY factors.
 //
-// One workgroup (4 waves) per (chunk, head).  With G the chunk-local
+// One workgroup (8 waves) per (chunk, head).  With G the chunk-local
 // inclusive cumsum of g, Gamma = exp(G), rows i, j of the chunk, and the
 // padding convention q = k = v = 0, g = 0, beta = 0 past a partial chunk's
 // end (so every quantity below is exactly zero or exactly carried there):
@@ -16,19 +16,27 @@
 // no row-serial elimination), section 6.1 (cumsum fused in), section 6.2
 // (what the recurrence consumes), section 6.3 (no backward-only columns).
 //
-// Strip-GEMMs.  Aqk and L are built from 16x16 blocks (a, b), a >= b.  Block
-// b's reference row r_b = 16 b + 7 (its midpoint) splits each factor as
-//   exp(G_i - G_j) = exp(G_i - G_{r_b}) * exp(G_{r_b} - G_j),
-// so with g in [-5, 0] each factor stays within 8 * 5 = 40 nats (57.7 bits,
-// well inside the bf16/fp32 exponent range) and rows i past block b only see
-// decay.  Operands are split into hi + lo bf16 and multiplied as
-// hi*hi + hi*lo + lo*hi on v_mfma_f32_16x16x32_bf16.
+// Strip factors.  Subblock a (rows 16a..16a+15) is referenced at its
+// midpoint r_a = 16a + 7.  Per element, E1 = exp(G_i - G_{r(i)}) and
+// E2 = 1/E1 = exp(G_{r(i)} - G_i) stay within 8 * 5 = 40 nats (57.7 bits)
+// because g >= -5, and
+//   exp(G_i - G_j) = E1_i * exp(G_{r_a} - G_{r_b}) * E2_j    (i in a, j in b),
+// where the middle factor C_ab <= 1 is one value per channel.  So with
+// q^ = q*E1, k^ = k*E1 and k~ = k*E2 computed once per element,
+//   Aqk block (a,b) = q^_a (k~_b * C_ab)^T,   L block (a,b) = k^_a (k~_b * C_ab)^T.
+// The Aqk strips use hi + lo bf16 on both operands (hi*hi + hi*lo + lo*hi);
+// the L strips feed an fp32 inverse whose result is rounded again, so plain
+// bf16 operands are enough there.  Gamma = E1 * exp(G_{r_a}) and
+// exp(G_last - G_j) = E2_j * exp(G_last - G_{r_b}) likewise need no further
+// per-element exponentials.
 //
 // Inverse.  The four diagonal 16x16 blocks use the finite Neumann product
 // (I + X)(I + X^2)(I + X^4)(I + X^8) with X = -L_aa, exact because X is
 // strictly lower (X^16 = 0); the off-diagonal blocks are merged as
 // T_ab = -T_aa sum_{c=b}^{a-1} L_ac T_cb, one block diagonal at a time.  All
-// of it runs in fp32 on v_mfma_f32_16x16x4_f32.
+// of it runs in fp32 on v_mfma_f32_16x16x4_f32.  While waves 0-3 invert the
+// diagonal blocks, waves 4-7 write the q*Gamma and kg fragments, which do
+// not depend on T.
 #include "kda_cumsum.h"
 #include "kda_internal.h"
 #include "kda_launch.h"
@@ -37,22 +45,43 @@ namespace kda {
 
 namespace {
 
-constexpr int QK_LD = 136;  // bf16 row stride in LDS (128 + 8 pad)
-constexpr int G_LD = 132;   // fp32 row stride (128 + 4 pad)
-constexpr int LT_LD = 68;   // fp32 row stride of the 64 x 64 L and T
-constexpr int Y_LD = 17;    // 16 x 16 scratch row stride
+constexpr int NT = INTRA_THREADS;  // 8 waves
+constexpr int Y_LD = 17;           // 16 x 16 scratch row stride
+
+// Row-major [64][128] tiles with their 16-byte chunks XOR-swizzled by the row
+// (chunk' = chunk ^ (row & 7)), so that the 16-byte fragment reads of 8
+// consecutive rows hit different LDS banks.
+__device__ __forceinline__ int sw_bf16(int row, int ch) {  // bf16 element index
+  return row * DK + ((((ch >> 3) ^ (row & 7)) << 3) | (ch & 7));
+}
+__device__ __forceinline__ int sw_f32(int row, int ch) {  // fp32 element index
+  return row * DK + ((((ch >> 2) ^ (row & 7)) << 2) | (ch & 3));
+}
+// The 64 x 64 fp32 L and T: 16-byte chunks swizzled by (row & 15), so the
+// 16 rows an MFMA operand read touches land in different banks.
+__device__ __forceinline__ int sw_lt(int row, int col) {
+  return row * BT + ((((col >> 2) ^ (row & 15)) << 2) | (col & 3));
+}
+
+// Per-channel tables: R[a] = exp(G_{r_a}), Q[b] = exp(G_last - G_{r_b}),
+// C[p] = exp(G_{r_a} - G_{r_b}) for the six off-diagonal pairs, and gamma.
+constexpr int TAB_R = 0, TAB_Q = 4, TAB_C = 8, TAB_GAM = 14, TAB_ROWS = 15;
+__device__ constexpr int OFF_A[6] = {1, 2, 2, 3, 3, 3};
+__device__ constexpr int OFF_B[6] = {0, 0, 1, 0, 1, 2};
 
 struct __align__(16) IntraSmem {
-  bf16_t q[BT][QK_LD];
-  bf16_t k[BT][QK_LD];
-  bf16_t v[BT][QK_LD];
-  float G[BT][G_LD];
-  float L[BT][LT_LD];
-  float T[BT][LT_LD];
+  bf16_t qh[BT * DK];   // q^ hi
+  bf16_t ql[BT * DK];   // q^ lo
+  bf16_t kh[BT * DK];   // k^ (bf16)
+  bf16_t v[BT * DK];    // v
+  float kt[BT * DK];    // k~ (fp32); holds the cumsum scratch before that
+  float G[BT * DK];     // G; then L (first 64 x 64) and T (next 64 x 64)
+  float tab[TAB_ROWS][DK];
   float Y[4][16][Y_LD];
   float beta[BT];
-  float tot[8][DK];
 };
+static_assert(2 * BT * BT <= BT * DK, "L and T fit where G was");
+static_assert(sizeof(IntraSmem) <= 160 * 1024, "fits the CU's LDS");
 
 // The six (token tile, token slab) pairs of a 64 x 64 lower-triangular
 // operand that hold any j <= i; index = AQK_IDX(mt, s).
@@ -66,9 +95,11 @@ __device__ __forceinline__ void store_bf16x8(uint8_t *p, const bf16x8 &x) {
   *reinterpret_cast<bf16x8 *>(p) = x;
 }
 
+__device__ __forceinline__ float bf(uint16_t b) { return bf16_bits_to_f32(b); }
+
 }  // namespace
 
-__global__ __launch_bounds__(256) void intra_kernel(IntraArgs a) {
+__global__ __launch_bounds__(NT) void intra_kernel(IntraArgs a) {
   __shared__ IntraSmem sm;
   const int64_t c = blockIdx.x / a.H;
   const int h = blockIdx.x % a.H;
@@ -81,58 +112,112 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraArgs a) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, nn = l & 15, grp = l >> 4;
   uint8_t *blk = a.blocks + ((int64_t)h * a.nc_max + c) * BLOCK_BYTES;
+  float *Ls = sm.G;                 // after the factors are built
+  float *Ts = sm.G + BT * BT;
 
-  // ---- q, k, v, beta into LDS (zero past the chunk end); G by cumsum ----
+  // ---- loads: thread t owns row er = t / 8 and the 4-channel chunks
+  // c = (t % 8) + 8 kk, kk = 0..3 (8 lanes cover 8 consecutive chunks, which
+  // keeps the LDS accesses below free of bank conflicts); q, k stay in
+  // registers, v goes to LDS, beta; then the chunk-local cumsum of g ----
+  const int er = tid >> 3;
+  const int ec = tid & 7;
+  uint2 q4[4], k4[4];
+  {
+    const bool ok = er < n;
+    const int64_t off = ((t0 + er) * a.H + h) * DK;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int ci = tid + 256 * it, row = ci >> 4, c16 = ci & 15;
-    uint4 vq = make_uint4(0, 0, 0, 0), vk = vq, vv = vq;
-    if (row < n) {
-      const int64_t off = ((t0 + row) * a.H + h) * DK + c16 * 8;
-      vq = *reinterpret_cast<const uint4 *>(a.q + off);
-      vk = *reinterpret_cast<const uint4 *>(a.k + off);
-      vv = *reinterpret_cast<const uint4 *>(a.v + off);
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ch = 4 * (ec + 8 * kk);
+      q4[kk] = ok ? *reinterpret_cast<const uint2 *>(a.q + off + ch) : make_uint2(0, 0);
+      k4[kk] = ok ? *reinterpret_cast<const uint2 *>(a.k + off + ch) : make_uint2(0, 0);
+      const uint2 v4 = ok ? *reinterpret_cast<const uint2 *>(a.v + off + ch) : make_uint2(0, 0);
+      *reinterpret_cast<uint2 *>(&sm.v[sw_bf16(er, ch)]) = v4;
     }
-    *reinterpret_cast<uint4 *>(&sm.q[row][c16 * 8]) = vq;
-    *reinterpret_cast<uint4 *>(&sm.k[row][c16 * 8]) = vk;
-    *reinterpret_cast<uint4 *>(&sm.v[row][c16 * 8]) = vv;
   }
   if (tid < BT) sm.beta[tid] = tid < n ? a.beta[(t0 + tid) * a.H + h] : 0.f;
-  chunk_gate_cumsum<G_LD>(a.g, t0, n, a.H, h, sm.G, sm.tot);
+  chunk_gate_cumsum<NT>(a.g, t0, n, a.H, h, sm.G, sw_f32, sm.kt);
   __syncthreads();
 
-  // ---- Aqk^T and L blocks by hi/lo strip-GEMMs ----
+  // ---- per-channel tables and per-element factors ----
+  for (int idx = tid; idx < TAB_ROWS * DK; idx += NT) {
+    const int tb = idx / DK, ch = idx % DK;
+    float val;
+    if (tb < TAB_Q) {
+      val = exp_nat(sm.G[sw_f32(SB * tb + SB_REF, ch)]);
+    } else if (tb < TAB_C) {
+      val = exp_nat(sm.G[sw_f32(BT - 1, ch)] - sm.G[sw_f32(SB * (tb - TAB_Q) + SB_REF, ch)]);
+    } else if (tb < TAB_GAM) {
+      const int p = tb - TAB_C;
+      val = exp_nat(sm.G[sw_f32(SB * OFF_A[p] + SB_REF, ch)] -
+                    sm.G[sw_f32(SB * OFF_B[p] + SB_REF, ch)]);
+    } else {
+      val = exp_nat(sm.G[sw_f32(BT - 1, ch)]);
+    }
+    sm.tab[tb][ch] = val;
+  }
   {
-    constexpr int PA[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-    constexpr int PB[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-    for (int p = w; p < 10; p += 4) {
-      const int ba = PA[p], bb = PB[p];
-      const int rref = SB * bb + SB_REF;
-      const int j = SB * bb + nn;  // row of the column-side factor k~
-      const int i = SB * ba + nn;  // row of the row-side factors q~, k^
+    const int rr = SB * (er / SB) + SB_REF;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ch = 4 * (ec + 8 * kk);
+      const float4 gi = *reinterpret_cast<const float4 *>(&sm.G[sw_f32(er, ch)]);
+      const float4 gr = *reinterpret_cast<const float4 *>(&sm.G[sw_f32(rr, ch)]);
+      const float d[4] = {gi.x - gr.x, gi.y - gr.y, gi.z - gr.z, gi.w - gr.w};
+      const uint16_t *qb = reinterpret_cast<const uint16_t *>(&q4[kk]);
+      const uint16_t *kb = reinterpret_cast<const uint16_t *>(&k4[kk]);
+      bf16x4 qhv, qlv, khv;
+      float ktv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float e1 = exp_nat(d[e]), e2 = exp_nat(-d[e]);
+        split_bf16(bf(qb[e]) * e1, qhv, qlv, e);
+        khv[e] = (bf16_t)(bf(kb[e]) * e1);
+        ktv[e] = bf(kb[e]) * e2;
+      }
+      *reinterpret_cast<bf16x4 *>(&sm.qh[sw_bf16(er, ch)]) = qhv;
+      *reinterpret_cast<bf16x4 *>(&sm.ql[sw_bf16(er, ch)]) = qlv;
+      *reinterpret_cast<bf16x4 *>(&sm.kh[sw_bf16(er, ch)]) = khv;
+      *reinterpret_cast<float4 *>(&sm.kt[sw_f32(er, ch)]) = make_float4(ktv[0], ktv[1], ktv[2], ktv[3]);
+    }
+  }
+  __syncthreads();
+
+  // ---- Aqk^T and L blocks: waves 0-5 one off-diagonal pair each, waves 6
+  // and 7 two diagonal pairs each ----
+  {
+    const int npairs = w < 6 ? 1 : 2;
+    for (int pi = 0; pi < npairs; ++pi) {
+      const int ba = w < 6 ? OFF_A[w] : (w - 6) * 2 + pi;
+      const int bb = w < 6 ? OFF_B[w] : ba;
+      const float *cab = w < 6 ? sm.tab[TAB_C + w] : nullptr;
+      const int j = SB * bb + nn;  // column-side rows (k~ C_ab)
+      const int i = SB * ba + nn;  // row-side rows (q^, k^)
       f32x4 accA = zero4(), accL = zero4();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int ch0 = 32 * s + 8 * grp;
-        bf16x8 kth, ktl, qth, qtl, krh, krl;
+        const float4 k0 = *reinterpret_cast<const float4 *>(&sm.kt[sw_f32(j, ch0)]);
+        const float4 k1 = *reinterpret_cast<const float4 *>(&sm.kt[sw_f32(j, ch0 + 4)]);
+        float kv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+        if (cab) {
+          const float4 c0 = *reinterpret_cast<const float4 *>(&cab[ch0]);
+          const float4 c1 = *reinterpret_cast<const float4 *>(&cab[ch0 + 4]);
+          const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ch = ch0 + e;
-          const float Gr = sm.G[rref][ch], Gj = sm.G[j][ch], Gi = sm.G[i][ch];
-          const float fk = exp_nat(Gr - Gj);
-          const float fq = exp_nat(Gi - Gr);
-          split_bf16((float)sm.k[j][ch] * fk, kth, ktl, e);
-          split_bf16((float)sm.q[i][ch] * fq, qth, qtl, e);
-          split_bf16((float)sm.k[i][ch] * fq, krh, krl, e);
+          for (int e = 0; e < 8; ++e) kv[e] *= cv[e];
         }
-        // Aqk^T block: rows j (A = k~), columns i (B = q~)
-        accA = mfma_bf16(kth, qth, accA);
-        accA = mfma_bf16(kth, qtl, accA);
-        accA = mfma_bf16(ktl, qth, accA);
-        // L block: rows i (A = k^), columns j (B = k~)
-        accL = mfma_bf16(krh, kth, accL);
-        accL = mfma_bf16(krh, ktl, accL);
-        accL = mfma_bf16(krl, kth, accL);
+        bf16x8 kth, ktl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split_bf16(kv[e], kth, ktl, e);
+        const bf16x8 qhv = *reinterpret_cast<const bf16x8 *>(&sm.qh[sw_bf16(i, ch0)]);
+        const bf16x8 qlv = *reinterpret_cast<const bf16x8 *>(&sm.ql[sw_bf16(i, ch0)]);
+        const bf16x8 khv = *reinterpret_cast<const bf16x8 *>(&sm.kh[sw_bf16(i, ch0)]);
+        // Aqk^T block: rows j (A = k~), columns i (B = q^), hi/lo
+        accA = mfma_bf16(kth, qhv, accA);
+        accA = mfma_bf16(kth, qlv, accA);
+        accA = mfma_bf16(ktl, qhv, accA);
+        // L block: rows i (A = k^), columns j (B = k~), bf16
+        accL = mfma_bf16(khv, kth, accL);
       }
       // Aqk^T: lane holds [j = 16bb + 4grp + r][i = 16ba + nn]; it becomes half
       // (bb & 1) of the recurrence's Aqk fragment (mt = ba, s = bb >> 1).
@@ -156,98 +241,174 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int il = 4 * grp + r;
         const bool keep = (ba > bb) || (nn < il);
-        sm.L[SB * ba + il][SB * bb + nn] = keep ? accL[r] * sm.beta[SB * ba + il] : 0.f;
+        Ls[sw_lt(SB * ba + il, SB * bb + nn)] = keep ? accL[r] * sm.beta[SB * ba + il] : 0.f;
       }
     }
   }
   __syncthreads();
 
-  // ---- diagonal blocks of T: Neumann product, wave w owns block w ----
-  {
+  if (w < 4) {
+    // ---- diagonal block w of T: Neumann product, wave-local ----
     const int d0 = SB * w;
     float(*Y)[Y_LD] = sm.Y[w];
     f32x4 P;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * grp + r;
-      const float x = (nn < m) ? -sm.L[d0 + m][d0 + nn] : 0.f;
+      const float x = (nn < m) ? -Ls[sw_lt(d0 + m, d0 + nn)] : 0.f;
       Y[m][nn] = x;
       P[r] = (nn == m) ? 1.f : x;
-      sm.T[d0 + m][d0 + nn] = P[r];
+      Ts[sw_lt(d0 + m, d0 + nn)] = P[r];
     }
-    __syncthreads();
+    // only this wave touches Y[w] and this diagonal block; LDS operations of
+    // a wave complete in order, so ordering the accesses suffices
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     for (int it = 0; it < 3; ++it) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) acc = mfma_f32(Y[nn][4 * s4 + grp], Y[4 * s4 + grp][nn], acc);
-      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int r = 0; r < 4; ++r) Y[4 * grp + r][nn] = acc[r];
-      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
       acc = P;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4)
-        acc = mfma_f32(sm.T[d0 + nn][d0 + 4 * s4 + grp], Y[4 * s4 + grp][nn], acc);
-      __syncthreads();
+        acc = mfma_f32(Ts[sw_lt(d0 + nn, d0 + 4 * s4 + grp)], Y[4 * s4 + grp][nn], acc);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
       P = acc;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.T[d0 + 4 * grp + r][d0 + nn] = acc[r];
-      __syncthreads();
+      for (int r = 0; r < 4; ++r) Ts[sw_lt(d0 + 4 * grp + r, d0 + nn)] = acc[r];
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+  } else {
+    // ---- waves 4-7: qg fragments (token tile u) and kg^T fragments (key
+    // tiles 2u, 2u+1), which do not depend on T ----
+    const int u = w - 4;
+    {
+      const int i = SB * u + nn;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 f;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int ch = 32 * s + 16 * hh + 4 * grp;
+          const bf16x4 qhv = *reinterpret_cast<const bf16x4 *>(&sm.qh[sw_bf16(i, ch)]);
+          const bf16x4 qlv = *reinterpret_cast<const bf16x4 *>(&sm.ql[sw_bf16(i, ch)]);
+          const float4 rv = *reinterpret_cast<const float4 *>(&sm.tab[TAB_R + u][ch]);
+          const float rr[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            f[4 * hh + e] = (bf16_t)(a.scale * ((float)qhv[e] + (float)qlv[e]) * rr[e]);
+        }
+        store_bf16x8(blk + OFF_QG + ((u * 4 + s) * 64 + l) * 16, f);
+      }
+    }
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int mtc = 2 * u + q2;
+      const int ch = 16 * mtc + nn;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bf16x8 f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int jj = 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3);
+          f[e] = (bf16_t)(sm.kt[sw_f32(jj, ch)] * sm.tab[TAB_Q + (jj >> 4)][ch]);
+        }
+        store_bf16x8(blk + OFF_KGT + ((mtc * 2 + s) * 64 + l) * 16, f);
+      }
+    }
+    if (u == 0) {
+      const float2 gv = *reinterpret_cast<const float2 *>(&sm.tab[TAB_GAM][2 * l]);
+      *reinterpret_cast<float2 *>(blk + OFF_GAM + 8 * l) = gv;
     }
   }
+  __syncthreads();
 
   // ---- off-diagonal blocks: T_ab = -T_aa sum_{c=b}^{a-1} L_ac T_cb ----
   for (int d = 1; d < 4; ++d) {
     const bool act = w < 4 - d;
     const int ba = w + d, bb = w;
-    float(*Y)[Y_LD] = sm.Y[w];
+    float(*Y)[Y_LD] = sm.Y[w & 3];
     if (act) {
       f32x4 acc = zero4();
       for (int cb = bb; cb < ba; ++cb) {
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4)
-          acc = mfma_f32(sm.L[SB * ba + nn][SB * cb + 4 * s4 + grp],
-                         sm.T[SB * cb + 4 * s4 + grp][SB * bb + nn], acc);
+          acc = mfma_f32(Ls[sw_lt(SB * ba + nn, SB * cb + 4 * s4 + grp)],
+                         Ts[sw_lt(SB * cb + 4 * s4 + grp, SB * bb + nn)], acc);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) Y[4 * grp + r][nn] = acc[r];
-    }
-    __syncthreads();
-    if (act) {
-      f32x4 acc = zero4();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      acc = zero4();
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4)
-        acc = mfma_f32(sm.T[SB * ba + nn][SB * ba + 4 * s4 + grp], Y[4 * s4 + grp][nn], acc);
+        acc = mfma_f32(Ts[sw_lt(SB * ba + nn, SB * ba + 4 * s4 + grp)], Y[4 * s4 + grp][nn], acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.T[SB * ba + 4 * grp + r][SB * bb + nn] = -acc[r];
+      for (int r = 0; r < 4; ++r) Ts[sw_lt(SB * ba + 4 * grp + r, SB * bb + nn)] = -acc[r];
     }
     __syncthreads();
   }
 
-  // ---- T' = T diag(beta) as hi/lo A fragments (rows i, 8 columns j) ----
+  // ---- T' = T diag(beta) as hi/lo A fragments (rows i, 8 columns j),
+  // built once into LDS where q^ was: waves 0-5 one fragment each ----
+  bf16_t *tfr = sm.qh;  // [hi: 6 x 64 lanes x 8][lo: 6 x 64 x 8]
+  if (w < 6) {
+    const int x = w;
+    const int i = SB * LT_MT[x] + nn;
+    const int j0 = 32 * LT_S[x] + 8 * grp;
+    const float4 t0v = *reinterpret_cast<const float4 *>(&Ts[sw_lt(i, j0)]);
+    const float4 t1v = *reinterpret_cast<const float4 *>(&Ts[sw_lt(i, j0 + 4)]);
+    const float4 b0v = *reinterpret_cast<const float4 *>(&sm.beta[j0]);
+    const float4 b1v = *reinterpret_cast<const float4 *>(&sm.beta[j0 + 4]);
+    const float tv[8] = {t0v.x, t0v.y, t0v.z, t0v.w, t1v.x, t1v.y, t1v.z, t1v.w};
+    const float bv[8] = {b0v.x, b0v.y, b0v.z, b0v.w, b1v.x, b1v.y, b1v.z, b1v.w};
+    bf16x8 fh, fl;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split_bf16((j0 + e <= i) ? tv[e] * bv[e] : 0.f, fh, fl, e);
+    *reinterpret_cast<bf16x8 *>(&tfr[(x * 64 + l) * 8]) = fh;
+    *reinterpret_cast<bf16x8 *>(&tfr[((6 + x) * 64 + l) * 8]) = fl;
+  }
+  __syncthreads();
   bf16x8 th[6], tl[6];
 #pragma unroll
   for (int x = 0; x < 6; ++x) {
-    const int i = SB * LT_MT[x] + nn;
-    const int j0 = 32 * LT_S[x] + 8 * grp;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int jj = j0 + e;
-      const float val = (jj <= i) ? sm.T[i][jj] * sm.beta[jj] : 0.f;
-      split_bf16(val, th[x], tl[x], e);
-    }
+    th[x] = *reinterpret_cast<const bf16x8 *>(&tfr[(x * 64 + l) * 8]);
+    tl[x] = *reinterpret_cast<const bf16x8 *>(&tfr[((6 + x) * 64 + l) * 8]);
   }
 
-  // ---- U = T' V: wave w writes value tiles nt = 2w, 2w+1 (C layout) ----
-#pragma unroll
-  for (int q2 = 0; q2 < 2; ++q2) {
-    const int nt = 2 * w + q2;
-    const int col = 16 * nt + nn;
+  // Transposed LDS read of a row-major bf16 tile (ds_read_b64_tr_b16): within
+  // each group of 16 lanes, lane j addresses row r0 + j/4, columns
+  // c0 + 4 (j%4) .. +3, and lane i receives tile[r0 + 0..3][c0 + i].  Two
+  // such reads give a B fragment's 8 consecutive k rows for column c0 + nn.
+  auto tr4 = [&](const bf16_t *tile, int r0, int c0) -> bf16x4 {
+    const bf16_t *p = &tile[sw_bf16(r0 + (nn >> 2), c0 + 4 * (nn & 3))];
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4 *)(p));
+  };
+
+  // ---- U = T' V: wave w writes value tile nt = w (C layout) ----
+  {
+    const int nt = w;
     bf16x8 vb[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < 2; ++s) {
+      const bf16x4 lo4 = tr4(sm.v, 32 * s + 8 * grp, 16 * nt);
+      const bf16x4 hi4 = tr4(sm.v, 32 * s + 8 * grp + 4, 16 * nt);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vb[s][e] = sm.v[32 * s + 8 * grp + e][col];
+      for (int e = 0; e < 4; ++e) {
+        vb[s][e] = lo4[e];
+        vb[s][4 + e] = hi4[e];
+      }
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       f32x4 acc = zero4();
@@ -257,35 +418,38 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraArgs a) {
         acc = mfma_bf16(th[x], vb[s], acc);
         acc = mfma_bf16(tl[x], vb[s], acc);
       }
-      bf16x4 u;
+      bf16x4 uv;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) u[r] = (bf16_t)acc[r];
-      store_bf16x4(blk + OFF_U + ((nt * 4 + mt) * 64 + l) * 8, u);
+      for (int r = 0; r < 4; ++r) uv[r] = (bf16_t)acc[r];
+      store_bf16x4(blk + OFF_U + ((nt * 4 + mt) * 64 + l) * 8, uv);
     }
   }
 
-  // ---- W^T = (K*Gamma)^T T'^T: wave w owns key tiles 2w, 2w+1 ----
-#pragma unroll
-  for (int q2 = 0; q2 < 2; ++q2) {
-    const int mtc = 2 * w + q2;
+  // ---- W^T = (K*Gamma)^T T'^T: wave w owns key tile w ----
+  {
+    const int mtc = w;
     const int ch = 16 * mtc + nn;
-    bf16x8 kh[2], kl[2];
+    bf16x8 kgm[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < 2; ++s) {
+      // rows 32s + 8grp .. +7 all lie in subblock 2s + grp/2
+      const float rv = sm.tab[TAB_R + 2 * s + (grp >> 1)][ch];
+      const bf16x4 lo4 = tr4(sm.kh, 32 * s + 8 * grp, 16 * mtc);
+      const bf16x4 hi4 = tr4(sm.kh, 32 * s + 8 * grp + 4, 16 * mtc);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int jj = 32 * s + 8 * grp + e;
-        split_bf16((float)sm.k[jj][ch] * exp_nat(sm.G[jj][ch]), kh[s], kl[s], e);
+      for (int e = 0; e < 4; ++e) {
+        kgm[s][e] = (bf16_t)((float)lo4[e] * rv);
+        kgm[s][4 + e] = (bf16_t)((float)hi4[e] * rv);
       }
+    }
 #pragma unroll
     for (int nti = 0; nti < 4; ++nti) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int s = 0; s <= (nti >> 1); ++s) {
         const int x = AQK_IDX(nti, s);
-        acc = mfma_bf16(kh[s], th[x], acc);
-        acc = mfma_bf16(kh[s], tl[x], acc);
-        acc = mfma_bf16(kl[s], th[x], acc);
+        acc = mfma_bf16(kgm[s], th[x], acc);
+        acc = mfma_bf16(kgm[s], tl[x], acc);
       }
       // lane holds W^T[16 mtc + 4grp + r][16 nti + nn] -> -W, half (mtc & 1)
       // of the fragment (token tile nti, key slab mtc >> 1)
@@ -295,48 +459,11 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraArgs a) {
       store_bf16x4(blk + OFF_WN + ((nti * 4 + (mtc >> 1)) * 64 + l) * 16 + (mtc & 1) * 8, wv);
     }
   }
-
-  // ---- qg = scale q Gamma fragments: wave w owns token tile w ----
-  {
-    const int i = SB * w + nn;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ch = 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3);
-        f[e] = (bf16_t)(a.scale * (float)sm.q[i][ch] * exp_nat(sm.G[i][ch]));
-      }
-      store_bf16x8(blk + OFF_QG + ((w * 4 + s) * 64 + l) * 16, f);
-    }
-  }
-
-  // ---- kg^T fragments: wave w owns key tiles 2w, 2w+1 ----
-#pragma unroll
-  for (int q2 = 0; q2 < 2; ++q2) {
-    const int mtc = 2 * w + q2;
-    const int ch = 16 * mtc + nn;
-    const float Glast = sm.G[BT - 1][ch];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int jj = 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3);
-        f[e] = (bf16_t)((float)sm.k[jj][ch] * exp_nat(Glast - sm.G[jj][ch]));
-      }
-      store_bf16x8(blk + OFF_KGT + ((mtc * 2 + s) * 64 + l) * 16, f);
-    }
-  }
-
-  if (tid < DK) {
-    *reinterpret_cast<float *>(blk + OFF_GAM + tid * 4) = exp_nat(sm.G[BT - 1][tid]);
-  }
 }
 
 hipError_t launch_intra(const IntraArgs &a, hipStream_t stream) {
   if (a.nc_max <= 0) return hipSuccess;
-  hipLaunchKernelGGL(intra_kernel, dim3((unsigned)(a.nc_max * a.H)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(intra_kernel, dim3((unsigned)(a.nc_max * a.H)), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -6,12 +6,11 @@
 //     v_new = U - W h
 //     o     = qg h + Aqk v_new              (reads the entry state h)
 //     h     = Diag(gamma) h + kg^T v_new
-// The 128 value columns of the state are independent, so each chain is
-// split over 4 single-wave workgroups of 32 columns each.  A wave keeps its
-// [128, 32] fp32 slice of the state in 16 MFMA C tiles for the whole
-// sequence; the state and v_new are fed back to the MFMAs as B operands
-// straight from their C tiles (bf16), in the permuted k order the
-// intra-chunk kernel wrote its A fragments in.
+// The 128 value columns of the state are independent, so each of the 4 waves
+// of a chain's workgroup keeps a [128, 32] fp32 slice of the state in 16 MFMA
+// C tiles for the whole sequence; the state and v_new are fed back to the
+// MFMAs as B operands straight from their C tiles (bf16), in the permuted k
+// order the intra-chunk kernel wrote its A fragments in.
 #include "kda_internal.h"
 #include "kda_launch.h"
 
@@ -26,19 +25,67 @@ __device__ __forceinline__ bf16x8 load_frag(const uint8_t *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }
 
+// o rows of one chunk: lane holds token 16 mt + nn and value columns
+// 16 (2w + q2) + 4 grp .. + 3, i.e. one 8-byte store per (mt, q2).
+__device__ __forceinline__ void store_o(const RecurArgs &a, int h, int w, int nn, int grp,
+                                        int64_t t0, int n, const bf16x4 (&ov)[4][2]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int row = 16 * mt + nn;
+    if (row < n) {
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+        *reinterpret_cast<bf16x4 *>(a.o + ((t0 + row) * a.H + h) * DV + 16 * (2 * w + q2) +
+                                    4 * grp) = ov[mt][q2];
+    }
+  }
+}
+
 }  // namespace
 
-// blockIdx -> (chain, quarter): the 4 quarters of a chain get block ids that
-// are equal mod 8, so the dispatcher puts them on the same XCD and they
-// share its L2 for the chain's intermediate blocks.
-__global__ __launch_bounds__(64) void recurrence_kernel(RecurArgs a) {
-  const int b = blockIdx.x;
-  const int xcd = b & 7, slot = b >> 3;
-  const int quarter = slot & 3;
-  const int64_t chain = (int64_t)(slot >> 2) * 8 + xcd;
+// One workgroup of 4 waves per (sequence, head) chain; wave w owns value
+// tiles 2w and 2w+1 (32 columns) of the state.  The chain's intermediate
+// blocks stream through two LDS buffers: while the waves compute chunk c from
+// one buffer, chunk c+1's block is copied global -> LDS into the other by
+// global_load_lds_dwordx4 (no register staging), so the four waves share one
+// copy of the fragments and the copy latency hides behind the MFMAs.
+constexpr int REC_THREADS = 256;
+constexpr int DMA_ROUND = REC_THREADS * 16;               // bytes per copy round
+constexpr int DMA_FULL = BLOCK_BYTES / DMA_ROUND;          // 19 full rounds
+constexpr int DMA_TAIL = BLOCK_BYTES - DMA_FULL * DMA_ROUND;  // 512 bytes
+static_assert(DMA_TAIL % 16 == 0 && DMA_TAIL <= 64 * 16, "tail fits one wave");
+
+__device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(
+      (const __attribute__((address_space(1))) void *)src,
+      (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+}
+
+// Copy one intermediate block into an LDS buffer: lane l of wave w copies
+// the 16 bytes at round * 4096 + w * 1024 + l * 16.  The copy is issued in
+// four parts spread over a chunk's MFMA work, so that the wave never stalls
+// on a burst of memory instructions.
+constexpr int DMA_PART = (DMA_FULL + 3) / 4;
+__device__ __forceinline__ void copy_block_part(const uint8_t *src, uint8_t *dst, int w, int l,
+                                                int part) {
+#pragma unroll
+  for (int r = part * DMA_PART; r < (part + 1) * DMA_PART && r < DMA_FULL; ++r)
+    dma16(src + r * DMA_ROUND + w * 1024 + l * 16, dst + r * DMA_ROUND + w * 1024);
+  if (part == 3 && w == 0 && l < DMA_TAIL / 16)
+    dma16(src + DMA_FULL * DMA_ROUND + l * 16, dst + DMA_FULL * DMA_ROUND);
+}
+__device__ __forceinline__ void copy_block(const uint8_t *src, uint8_t *dst, int w, int l) {
+#pragma unroll
+  for (int part = 0; part < 4; ++part) copy_block_part(src, dst, w, l, part);
+}
+
+__global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
+  __shared__ __align__(16) uint8_t lds[2][BLOCK_BYTES];
+  const int64_t chain = blockIdx.x;
   if (chain >= (int64_t)a.N * a.H) return;
   const int s = (int)(chain / a.H), h = (int)(chain % a.H);
-  const int l = threadIdx.x, nn = l & 15, grp = l >> 4;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, nn = l & 15, grp = l >> 4;
   // chunk range and token ranges are clamped so that a workspace that does
   // not hold a valid chunk table can never send this kernel out of bounds
   const int64_t nc_max = a.nc_max;
@@ -46,8 +93,9 @@ __global__ __launch_bounds__(64) void recurrence_kernel(RecurArgs a) {
   c_beg = c_beg < 0 ? 0 : (c_beg > nc_max ? nc_max : c_beg);
   c_end = c_end < c_beg ? c_beg : (c_end > nc_max ? nc_max : c_end);
   const int64_t st_base = ((int64_t)s * a.H + h) * DK * DV;
+  const uint8_t *chain_blocks = a.blocks + (int64_t)h * nc_max * BLOCK_BYTES;
 
-  // state slice: key tiles t = 0..7, value tiles 2*quarter + q2
+  // state slice: key tiles t = 0..7, value tiles 2w + q2
   f32x4 S[8][2];
 #pragma unroll
   for (int t = 0; t < 8; ++t)
@@ -56,17 +104,34 @@ __global__ __launch_bounds__(64) void recurrence_kernel(RecurArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * t + 4 * grp + r;
-        const int col = 16 * (2 * quarter + q2) + nn;
+        const int col = 16 * (2 * w + q2) + nn;
         S[t][q2][r] = a.h0 ? a.h0[st_base + row * DV + col] : 0.f;
       }
 
+  if (c_beg < c_end) copy_block(chain_blocks + c_beg * BLOCK_BYTES, lds[0], w, l);
+
+  // o of chunk c is stored at the start of chunk c+1, right after the next
+  // copy is issued, so that the store latency overlaps a whole chunk of work
+  // instead of the wait for that copy
+  bf16x4 o_pend[4][2];
+  int64_t o_t0 = 0;
+  int o_n = 0;
+
   for (int64_t c = c_beg; c < c_end; ++c) {
+    const int cur = (int)((c - c_beg) & 1);
+    // this thread's copies (and earlier stores) are done; after the barrier
+    // every thread's are, and nobody still reads the other buffer
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const bool more = c + 1 < c_end;
+    const uint8_t *next_src = chain_blocks + (c + 1) * BLOCK_BYTES;
+    uint8_t *next_dst = lds[cur ^ 1];
+    const uint8_t *blk = lds[cur];
     const int4 info = a.chunk_info[c];
     const int64_t t0 = info.x < 0 ? 0 : (info.x > a.T ? a.T : info.x);
     const int n = (int)(info.y < 0 ? 0 : (info.y > a.T - t0 ? a.T - t0 : info.y));
-    const uint8_t *blk = a.blocks + ((int64_t)h * a.nc_max + c) * BLOCK_BYTES;
 
-    // entry state as bf16 B operands (k slabs of 32 key rows)
+    // entry state as bf16 MFMA operands (k slabs of 32 key rows)
     bf16x8 hb[4][2];
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
@@ -75,34 +140,44 @@ __global__ __launch_bounds__(64) void recurrence_kernel(RecurArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) hb[s4][q2][e] = (bf16_t)S[2 * s4 + (e >> 2)][q2][e & 3];
 
-    // v_new starts from U; o from zero
-    f32x4 vn[4][2], oc[4][2];
+    // v_new starts from U (C layout: [token][value]); o^T from zero
+    f32x4 vn[4][2], ot[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
         const bf16x4 u = *reinterpret_cast<const bf16x4 *>(
-            blk + OFF_U + (((2 * quarter + q2) * 4 + mt) * 64 + l) * 8);
+            blk + OFF_U + (((2 * w + q2) * 4 + mt) * 64 + l) * 8);
 #pragma unroll
         for (int r = 0; r < 4; ++r) vn[mt][q2][r] = (float)u[r];
-        oc[mt][q2] = zero4();
+        ot[mt][q2] = zero4();
       }
 
-    // v_new += (-W) h ;  o += qg h
+    // v_new += (-W) h   and   o^T += h^T qg^T   (o is formed transposed so
+    // that each lane ends up with 4 consecutive value columns of one token).
+    // Fragments stream through a window of one key slab (8 fragments).
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int s4 = 0; s4 < 4; ++s4) {
+      // a quarter of the next chunk's copy (and, first, last chunk's o)
+      if (s4 == 0 && c > c_beg) store_o(a, h, w, nn, grp, o_t0, o_n, o_pend);
+      if (more) copy_block_part(next_src, next_dst, w, l, s4);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 fw[4], fq[4];
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const bf16x8 wn = load_frag(blk + OFF_WN + ((mt * 4 + s4) * 64 + l) * 16);
-        const bf16x8 qg = load_frag(blk + OFF_QG + ((mt * 4 + s4) * 64 + l) * 16);
+      for (int mt = 0; mt < 4; ++mt) {
+        fw[mt] = load_frag(blk + OFF_WN + ((mt * 4 + s4) * 64 + l) * 16);
+        fq[mt] = load_frag(blk + OFF_QG + ((mt * 4 + s4) * 64 + l) * 16);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2) {
-          vn[mt][q2] = mfma_bf16(wn, hb[s4][q2], vn[mt][q2]);
-          oc[mt][q2] = mfma_bf16(qg, hb[s4][q2], oc[mt][q2]);
+          vn[mt][q2] = mfma_bf16(fw[mt], hb[s4][q2], vn[mt][q2]);
+          ot[mt][q2] = mfma_bf16(hb[s4][q2], fq[mt], ot[mt][q2]);
         }
-      }
+    }
 
-    // v_new as bf16 B operands (k slabs of 32 tokens)
+    // v_new as bf16 operands (k slabs of 32 tokens)
     bf16x8 vb[2][2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
@@ -111,19 +186,7 @@ __global__ __launch_bounds__(64) void recurrence_kernel(RecurArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) vb[s2][q2][e] = (bf16_t)vn[2 * s2 + (e >> 2)][q2][e & 3];
 
-    // o += Aqk v_new  (Aqk in hi + lo bf16)
-#pragma unroll
-    for (int x = 0; x < AQK_FRAGS; ++x) {
-      const bf16x8 ah = load_frag(blk + OFF_AQK + (x * 64 + l) * 16);
-      const bf16x8 al = load_frag(blk + OFF_AQK + ((AQK_FRAGS + x) * 64 + l) * 16);
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        oc[LT_MT[x]][q2] = mfma_bf16(ah, vb[LT_S[x]][q2], oc[LT_MT[x]][q2]);
-        oc[LT_MT[x]][q2] = mfma_bf16(al, vb[LT_S[x]][q2], oc[LT_MT[x]][q2]);
-      }
-    }
-
-    // h <- Diag(gamma) h + kg^T v_new
+    // h <- Diag(gamma) h + kg^T v_new   (the serial dependency: first)
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const float4 gm = *reinterpret_cast<const float4 *>(blk + OFF_GAM + (16 * t + 4 * grp) * 4);
@@ -136,29 +199,45 @@ __global__ __launch_bounds__(64) void recurrence_kernel(RecurArgs a) {
       }
     }
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int tb = 0; tb < 8; tb += 4) {
+      bf16x8 fk[2][4];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 kg = load_frag(blk + OFF_KGT + ((t * 2 + s2) * 64 + l) * 16);
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) S[t][q2] = mfma_bf16(kg, vb[s2][q2], S[t][q2]);
-      }
+        for (int t = 0; t < 4; ++t)
+          fk[s2][t] = load_frag(blk + OFF_KGT + (((tb + t) * 2 + s2) * 64 + l) * 16);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2)
+            S[tb + t][q2] = mfma_bf16(fk[s2][t], vb[s2][q2], S[tb + t][q2]);
+    }
 
-    // o rows of this chunk (bf16, round to nearest even)
+    // o^T += v_new^T Aqk^T   (Aqk in hi + lo bf16)
+#pragma unroll
+    for (int x = 0; x < AQK_FRAGS; ++x) {
+      const bf16x8 fah = load_frag(blk + OFF_AQK + (x * 64 + l) * 16);
+      const bf16x8 fal = load_frag(blk + OFF_AQK + ((AQK_FRAGS + x) * 64 + l) * 16);
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        ot[LT_MT[x]][q2] = mfma_bf16(vb[LT_S[x]][q2], fah, ot[LT_MT[x]][q2]);
+        ot[LT_MT[x]][q2] = mfma_bf16(vb[LT_S[x]][q2], fal, ot[LT_MT[x]][q2]);
+      }
+    }
+
+    // o^T of this chunk as bf16 (nearest even), stored at the next chunk
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * mt + 4 * grp + r;
-          if (row < n) {
-            const bf16_t ov = (bf16_t)oc[mt][q2][r];
-            a.o[((t0 + row) * a.H + h) * DV + 16 * (2 * quarter + q2) + nn] =
-                __builtin_bit_cast(uint16_t, ov);
-          }
-        }
+        for (int r = 0; r < 4; ++r) o_pend[mt][q2][r] = (bf16_t)ot[mt][q2][r];
+    o_t0 = t0;
+    o_n = n;
   }
+  if (c_end > c_beg) store_o(a, h, w, nn, grp, o_t0, o_n, o_pend);
 
   if (a.hT) {
 #pragma unroll
@@ -168,7 +247,7 @@ __global__ __launch_bounds__(64) void recurrence_kernel(RecurArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * t + 4 * grp + r;
-          const int col = 16 * (2 * quarter + q2) + nn;
+          const int col = 16 * (2 * w + q2) + nn;
           a.hT[st_base + row * DV + col] = S[t][q2][r];
         }
   }
@@ -176,8 +255,7 @@ __global__ __launch_bounds__(64) void recurrence_kernel(RecurArgs a) {
 
 hipError_t launch_recurrence(const RecurArgs &a, hipStream_t stream) {
   const int64_t chains = (int64_t)a.N * a.H;
-  const int64_t blocks = (chains + 7) / 8 * 32;
-  hipLaunchKernelGGL(recurrence_kernel, dim3((unsigned)blocks), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(recurrence_kernel, dim3((unsigned)chains), dim3(REC_THREADS), 0, stream, a);
   return hipGetLastError();
 }
 

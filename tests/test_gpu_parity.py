@@ -184,3 +184,14 @@ def test_intra_then_recurrence_equals_fwd(dev):
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("gmul", [0.0, 0.01], ids=["g_zero", "weak_decay"])
+def test_weak_and_no_decay(dev, gmul):
+    # with little or no decay the state carries the whole history, the
+    # hardest case for the bf16 rounding budget
+    w = wl.small([700, 130, 64], H=2, seed=48, scale=1.0)
+    w.g = (w.g * np.float32(gmul)).astype(np.float32)
+    log(f"[case] decay scaled by {gmul}")
+    o, f = run_gpu(w, dev)
+    parity(o, f, *run_oracle(w), f"g*{gmul}")
