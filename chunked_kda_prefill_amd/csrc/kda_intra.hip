@@ -46,7 +46,6 @@ namespace kda {
 namespace {
 
 constexpr int NT = INTRA_THREADS;  // 8 waves
-constexpr int Y_LD = 17;           // 16 x 16 scratch row stride
 
 // Row-major [64][128] tiles with their 16-byte chunks XOR-swizzled by the row
 // (chunk' = chunk ^ (row & 7)), so that the 16-byte fragment reads of 8
@@ -77,7 +76,6 @@ struct __align__(16) IntraSmem {
   float kt[BT * DK];    // k~ (fp32); holds the cumsum scratch before that
   float G[BT * DK];     // G; then L (first 64 x 64) and T (next 64 x 64)
   float tab[TAB_ROWS][DK];
-  float Y[4][16][Y_LD];
   float beta[BT];
 };
 static_assert(2 * BT * BT <= BT * DK, "L and T fit where G was");
@@ -97,45 +95,80 @@ __device__ __forceinline__ void store_bf16x8(uint8_t *p, const bf16x8 &x) {
 
 __device__ __forceinline__ float bf(uint16_t b) { return bf16_bits_to_f32(b); }
 
+// 16 x 16 x 16 fp32 product from C-layout registers: At holds A^T and B holds
+// B (lane (nn, grp), element r = row 4grp + r, column nn); k runs over
+// 4 grp + s.  Returns acc + A B in the same layout.
+__device__ __forceinline__ f32x4 mm16(const f32x4 &At, const f32x4 &B, f32x4 acc) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = mfma_f32(At[s], B[s], acc);
+  return acc;
+}
+
 }  // namespace
 
-__global__ __launch_bounds__(NT) void intra_kernel(IntraArgs a) {
-  __shared__ IntraSmem sm;
-  const int64_t c = blockIdx.x / a.H;
-  const int h = blockIdx.x % a.H;
-  if (c >= a.chunk_first[a.N]) return;
-  const int4 info = a.chunk_info[c];
+// Inputs of one (chunk, head) unit, loaded into registers ahead of use.
+struct UnitInputs {
+  int64_t t0;
+  int n;
+  uint2 q4[4], k4[4], v4[4];  // row er, 4-channel chunks (ec + 8 kk)
+  float beta;                 // threads < 64: row tid
+  GateRows<NT> g;
+};
+
+__device__ __forceinline__ void load_unit(const IntraArgs &a, const int4 info, int h, int er, int ec,
+                                          UnitInputs &in) {
   // the chunk table is written by the same call; clamping keeps even a
   // corrupted one in bounds
-  const int64_t t0 = info.x < 0 ? 0 : (info.x > a.T ? a.T : info.x);
-  const int n = (int)(info.y < 0 ? 0 : (info.y > a.T - t0 ? a.T - t0 : (info.y > BT ? BT : info.y)));
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, nn = l & 15, grp = l >> 4;
-  uint8_t *blk = a.blocks + ((int64_t)h * a.nc_max + c) * BLOCK_BYTES;
-  float *Ls = sm.G;                 // after the factors are built
-  float *Ts = sm.G + BT * BT;
-
-  // ---- loads: thread t owns row er = t / 8 and the 4-channel chunks
-  // c = (t % 8) + 8 kk, kk = 0..3 (8 lanes cover 8 consecutive chunks, which
-  // keeps the LDS accesses below free of bank conflicts); q, k stay in
-  // registers, v goes to LDS, beta; then the chunk-local cumsum of g ----
-  const int er = tid >> 3;
-  const int ec = tid & 7;
-  uint2 q4[4], k4[4];
-  {
-    const bool ok = er < n;
-    const int64_t off = ((t0 + er) * a.H + h) * DK;
+  in.t0 = info.x < 0 ? 0 : (info.x > a.T ? a.T : info.x);
+  in.n = (int)(info.y < 0 ? 0 : (info.y > a.T - in.t0 ? a.T - in.t0 : (info.y > BT ? BT : info.y)));
+  const bool ok = er < in.n;
+  const int64_t off = ((in.t0 + er) * a.H + h) * DK;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int ch = 4 * (ec + 8 * kk);
-      q4[kk] = ok ? *reinterpret_cast<const uint2 *>(a.q + off + ch) : make_uint2(0, 0);
-      k4[kk] = ok ? *reinterpret_cast<const uint2 *>(a.k + off + ch) : make_uint2(0, 0);
-      const uint2 v4 = ok ? *reinterpret_cast<const uint2 *>(a.v + off + ch) : make_uint2(0, 0);
-      *reinterpret_cast<uint2 *>(&sm.v[sw_bf16(er, ch)]) = v4;
-    }
+  for (int kk = 0; kk < 4; ++kk) {
+    const int ch = 4 * (ec + 8 * kk);
+    in.q4[kk] = ok ? *reinterpret_cast<const uint2 *>(a.q + off + ch) : make_uint2(0, 0);
+    in.k4[kk] = ok ? *reinterpret_cast<const uint2 *>(a.k + off + ch) : make_uint2(0, 0);
+    in.v4[kk] = ok ? *reinterpret_cast<const uint2 *>(a.v + off + ch) : make_uint2(0, 0);
   }
-  if (tid < BT) sm.beta[tid] = tid < n ? a.beta[(t0 + tid) * a.H + h] : 0.f;
-  chunk_gate_cumsum<NT>(a.g, t0, n, a.H, h, sm.G, sw_f32, sm.kt);
+  const int tid = threadIdx.x;
+  in.beta = (tid < BT && tid < in.n) ? a.beta[(in.t0 + tid) * a.H + h] : 0.f;
+  gate_rows_load<NT>(a.g, in.t0, in.n, a.H, h, in.g);
+}
+
+// One (chunk, head) unit.  `nxt` receives the next unit's inputs, loaded
+// once this unit's own inputs are consumed.
+__device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, int64_t u,
+                                           int64_t units, UnitInputs &nxt) {
+  // threadIdx.x through an opaque move, so that address arithmetic derived
+  // from it stays inside the unit loop instead of being hoisted out of it
+  int tid;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+  const int w = tid >> 6, l = tid & 63, nn = l & 15, grp = l >> 4;
+  const int er = tid >> 3;  // element-phase row
+  const int ec = tid & 7;   // element-phase chunk lane: chunks ec + 8 kk
+  float *Ls = sm.G;         // after the factors are built
+  float *Ts = sm.G + BT * BT;
+  const int64_t c = u / a.H;
+  const int h = (int)(u % a.H);
+  // the next unit's chunk record, fetched now so that its data loads can be
+  // issued later without waiting on it
+  const int64_t un = u + gridDim.x;
+  const int4 info_next = un < units ? a.chunk_info[un / a.H] : make_int4(0, 0, 0, 0);
+  UnitInputs in = nxt;
+  const int n = in.n;
+  uint8_t *blk = a.blocks + ((int64_t)h * a.nc_max + c) * BLOCK_BYTES;
+  // every wave is done with the previous unit's LDS
+  __syncthreads();
+
+  // ---- stage v and beta, scan g into G; then start the next unit's loads
+  // thread t owns row er = t / 8 and the 4-channel chunks c = (t % 8) + 8 kk,
+  // kk = 0..3 (8 lanes cover 8 consecutive chunks, which keeps the LDS
+  // accesses below free of bank conflicts) ----
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    *reinterpret_cast<uint2 *>(&sm.v[sw_bf16(er, 4 * (ec + 8 * kk))]) = in.v4[kk];
+  if (tid < BT) sm.beta[tid] = in.beta;
+  gate_rows_scan<NT>(in.g, sm.G, sw_f32, sm.kt);
   __syncthreads();
 
   // ---- per-channel tables and per-element factors ----
@@ -163,8 +196,8 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs a) {
       const float4 gi = *reinterpret_cast<const float4 *>(&sm.G[sw_f32(er, ch)]);
       const float4 gr = *reinterpret_cast<const float4 *>(&sm.G[sw_f32(rr, ch)]);
       const float d[4] = {gi.x - gr.x, gi.y - gr.y, gi.z - gr.z, gi.w - gr.w};
-      const uint16_t *qb = reinterpret_cast<const uint16_t *>(&q4[kk]);
-      const uint16_t *kb = reinterpret_cast<const uint16_t *>(&k4[kk]);
+      const uint16_t *qb = reinterpret_cast<const uint16_t *>(&in.q4[kk]);
+      const uint16_t *kb = reinterpret_cast<const uint16_t *>(&in.k4[kk]);
       bf16x4 qhv, qlv, khv;
       float ktv[4];
 #pragma unroll
@@ -181,6 +214,9 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs a) {
     }
   }
   __syncthreads();
+
+  // ---- the current unit's inputs are consumed: start the next unit's loads
+  if (un < units) load_unit(a, info_next, (int)(un % a.H), er, ec, nxt);
 
   // ---- Aqk^T and L blocks: waves 0-5 one off-diagonal pair each, waves 6
   // and 7 two diagonal pairs each ----
@@ -248,44 +284,39 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs a) {
   __syncthreads();
 
   if (w < 4) {
-    // ---- diagonal block w of T: Neumann product, wave-local ----
+    // ---- diagonal block w of T: Neumann product in registers ----
+    // Every 16 x 16 matrix M lives in MFMA C layout (lane (nn, grp) holds
+    // M[4grp + r][nn], r = 0..3), next to its transpose.  With the k order
+    // k = 4 grp + s, a product A B is  sum_s mfma(At[s], B[s])  for A^T and B
+    // in that layout, so the chain needs no LDS round trips.
     const int d0 = SB * w;
-    float(*Y)[Y_LD] = sm.Y[w];
-    f32x4 P;
+    f32x4 YC, YtC, PC, PtC;  // X = -L_ww and X^T; P = I + X and P^T
+    {
+      const float4 row = *reinterpret_cast<const float4 *>(&Ls[sw_lt(d0 + nn, d0 + 4 * grp)]);
+      const float rv[4] = {row.x, row.y, row.z, row.w};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * grp + r;
-      const float x = (nn < m) ? -Ls[sw_lt(d0 + m, d0 + nn)] : 0.f;
-      Y[m][nn] = x;
-      P[r] = (nn == m) ? 1.f : x;
-      Ts[sw_lt(d0 + m, d0 + nn)] = P[r];
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * grp + r;
+        YC[r] = (nn < m) ? -Ls[sw_lt(d0 + m, d0 + nn)] : 0.f;
+        YtC[r] = (m < nn) ? -rv[r] : 0.f;
+        PC[r] = (m == nn) ? 1.f : YC[r];
+        PtC[r] = (m == nn) ? 1.f : YtC[r];
+      }
     }
-    // only this wave touches Y[w] and this diagonal block; LDS operations of
-    // a wave complete in order, so ordering the accesses suffices
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+#pragma unroll
     for (int it = 0; it < 3; ++it) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) acc = mfma_f32(Y[nn][4 * s4 + grp], Y[4 * s4 + grp][nn], acc);
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Y[4 * grp + r][nn] = acc[r];
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      acc = P;
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        acc = mfma_f32(Ts[sw_lt(d0 + nn, d0 + 4 * s4 + grp)], Y[4 * s4 + grp][nn], acc);
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      P = acc;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Ts[sw_lt(d0 + 4 * grp + r, d0 + nn)] = acc[r];
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      __builtin_amdgcn_wave_barrier();
+      const f32x4 Y2C = mm16(YtC, YC, zero4());    // Y Y
+      const f32x4 PnC = mm16(PtC, Y2C, PC);        // P + P Y^2
+      if (it < 2) {
+        const f32x4 Y2tC = mm16(YC, YtC, zero4());  // Y^T Y^T
+        PtC = mm16(Y2C, PtC, PtC);                  // P^T + (Y^2)^T P^T
+        YC = Y2C;
+        YtC = Y2tC;
+      }
+      PC = PnC;
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Ts[sw_lt(d0 + 4 * grp + r, d0 + nn)] = PC[r];
   } else {
     // ---- waves 4-7: qg fragments (token tile u) and kg^T fragments (key
     // tiles 2u, 2u+1), which do not depend on T ----
@@ -331,29 +362,26 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs a) {
   }
   __syncthreads();
 
-  // ---- off-diagonal blocks: T_ab = -T_aa sum_{c=b}^{a-1} L_ac T_cb ----
+  // ---- off-diagonal blocks: T_ab = -T_aa sum_{c=b}^{a-1} L_ac T_cb, one
+  // block diagonal d = a - b at a time (wave b computes block (b+d, b)) ----
   for (int d = 1; d < 4; ++d) {
-    const bool act = w < 4 - d;
-    const int ba = w + d, bb = w;
-    float(*Y)[Y_LD] = sm.Y[w & 3];
-    if (act) {
-      f32x4 acc = zero4();
+    if (w < 4 - d) {
+      const int ba = w + d, bb = w;
+      f32x4 MC = zero4();
       for (int cb = bb; cb < ba; ++cb) {
+        // A = L_ac: its transpose in C layout is row nn, 4 consecutive columns
+        const float4 lr = *reinterpret_cast<const float4 *>(&Ls[sw_lt(SB * ba + nn, SB * cb + 4 * grp)]);
+        const f32x4 LtC = {lr.x, lr.y, lr.z, lr.w};
+        f32x4 TC;
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
-          acc = mfma_f32(Ls[sw_lt(SB * ba + nn, SB * cb + 4 * s4 + grp)],
-                         Ts[sw_lt(SB * cb + 4 * s4 + grp, SB * bb + nn)], acc);
+        for (int r = 0; r < 4; ++r) TC[r] = Ts[sw_lt(SB * cb + 4 * grp + r, SB * bb + nn)];
+        MC = mm16(LtC, TC, MC);
       }
+      const float4 tr = *reinterpret_cast<const float4 *>(&Ts[sw_lt(SB * ba + nn, SB * ba + 4 * grp)]);
+      const f32x4 TaatC = {tr.x, tr.y, tr.z, tr.w};
+      const f32x4 TabC = mm16(TaatC, MC, zero4());
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Y[4 * grp + r][nn] = acc[r];
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      acc = zero4();
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        acc = mfma_f32(Ts[sw_lt(SB * ba + nn, SB * ba + 4 * s4 + grp)], Y[4 * s4 + grp][nn], acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Ts[sw_lt(SB * ba + 4 * grp + r, SB * bb + nn)] = -acc[r];
+      for (int r = 0; r < 4; ++r) Ts[sw_lt(SB * ba + 4 * grp + r, SB * bb + nn)] = -TabC[r];
     }
     __syncthreads();
   }
@@ -461,9 +489,31 @@ __global__ __launch_bounds__(NT) void intra_kernel(IntraArgs a) {
   }
 }
 
+// Persistent: one workgroup per CU walks the (chunk, head) units with a
+// stride of the grid size; the next unit's inputs are loaded into registers
+// while the current one computes, so HBM reads overlap the LDS/MFMA work.
+__global__ __launch_bounds__(NT) void intra_kernel(IntraArgs a) {
+  __shared__ IntraSmem sm;
+  int64_t nc = a.chunk_first[a.N];
+  nc = nc < 0 ? 0 : (nc > a.nc_max ? a.nc_max : nc);
+  const int64_t units = nc * a.H;
+  int64_t u = blockIdx.x;
+  if (u >= units) return;
+  UnitInputs nxt;
+  load_unit(a, a.chunk_info[u / a.H], (int)(u % a.H), threadIdx.x >> 3, threadIdx.x & 7, nxt);
+  for (; u < units; u += gridDim.x) intra_unit(a, sm, u, units, nxt);
+}
+
 hipError_t launch_intra(const IntraArgs &a, hipStream_t stream) {
   if (a.nc_max <= 0) return hipSuccess;
-  hipLaunchKernelGGL(intra_kernel, dim3((unsigned)(a.nc_max * a.H)), dim3(NT), 0, stream, a);
+  // one workgroup per compute unit (the LDS footprint allows no more)
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t units = a.nc_max * a.H;
+  const int64_t grid = units < cus ? units : cus;
+  hipLaunchKernelGGL(intra_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -131,6 +131,15 @@ __global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
     const int64_t t0 = info.x < 0 ? 0 : (info.x > a.T ? a.T : info.x);
     const int n = (int)(info.y < 0 ? 0 : (info.y > a.T - t0 ? a.T - t0 : info.y));
 
+    // fragments of -W and qg for key slab 0 (the rest are prefetched one
+    // slab ahead inside the loop below)
+    bf16x8 fw[4], fq[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      fw[mt] = load_frag(blk + OFF_WN + ((mt * 4 + 0) * 64 + l) * 16);
+      fq[mt] = load_frag(blk + OFF_QG + ((mt * 4 + 0) * 64 + l) * 16);
+    }
+
     // entry state as bf16 MFMA operands (k slabs of 32 key rows)
     bf16x8 hb[4][2];
 #pragma unroll
@@ -153,20 +162,41 @@ __global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
         ot[mt][q2] = zero4();
       }
 
+    // the state is no longer needed unscaled: apply Diag(gamma) now, while
+    // the MFMAs below run
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float4 gm = *reinterpret_cast<const float4 *>(blk + OFF_GAM + (16 * t + 4 * grp) * 4);
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        S[t][q2][0] *= gm.x;
+        S[t][q2][1] *= gm.y;
+        S[t][q2][2] *= gm.z;
+        S[t][q2][3] *= gm.w;
+      }
+    }
+
     // v_new += (-W) h   and   o^T += h^T qg^T   (o is formed transposed so
-    // that each lane ends up with 4 consecutive value columns of one token).
-    // Fragments stream through a window of one key slab (8 fragments).
+    // that each lane ends up with 4 consecutive value columns of one token)
+    bf16x8 fk[2][8];
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      // a quarter of the next chunk's copy (and, first, last chunk's o)
+      // one quarter of the next chunk's copy (and, first, last chunk's o)
       if (s4 == 0 && c > c_beg) store_o(a, h, w, nn, grp, o_t0, o_n, o_pend);
       if (more) copy_block_part(next_src, next_dst, w, l, s4);
-      __builtin_amdgcn_sched_barrier(0);
-      bf16x8 fw[4], fq[4];
+      bf16x8 nw[4], nq[4];
+      if (s4 < 3) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        fw[mt] = load_frag(blk + OFF_WN + ((mt * 4 + s4) * 64 + l) * 16);
-        fq[mt] = load_frag(blk + OFF_QG + ((mt * 4 + s4) * 64 + l) * 16);
+        for (int mt = 0; mt < 4; ++mt) {
+          nw[mt] = load_frag(blk + OFF_WN + ((mt * 4 + s4 + 1) * 64 + l) * 16);
+          nq[mt] = load_frag(blk + OFF_QG + ((mt * 4 + s4 + 1) * 64 + l) * 16);
+        }
+      } else {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            fk[s2][t] = load_frag(blk + OFF_KGT + ((t * 2 + s2) * 64 + l) * 16);
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -175,6 +205,13 @@ __global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
           vn[mt][q2] = mfma_bf16(fw[mt], hb[s4][q2], vn[mt][q2]);
           ot[mt][q2] = mfma_bf16(hb[s4][q2], fq[mt], ot[mt][q2]);
         }
+      if (s4 < 3) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          fw[mt] = nw[mt];
+          fq[mt] = nq[mt];
+        }
+      }
     }
 
     // v_new as bf16 operands (k slabs of 32 tokens)
@@ -187,45 +224,27 @@ __global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
         for (int e = 0; e < 8; ++e) vb[s2][q2][e] = (bf16_t)vn[2 * s2 + (e >> 2)][q2][e & 3];
 
     // h <- Diag(gamma) h + kg^T v_new   (the serial dependency: first)
+    bf16x8 fah[AQK_FRAGS], fal[AQK_FRAGS];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float4 gm = *reinterpret_cast<const float4 *>(blk + OFF_GAM + (16 * t + 4 * grp) * 4);
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        S[t][q2][0] *= gm.x;
-        S[t][q2][1] *= gm.y;
-        S[t][q2][2] *= gm.z;
-        S[t][q2][3] *= gm.w;
-      }
+    for (int x = 0; x < AQK_FRAGS; ++x) {
+      fah[x] = load_frag(blk + OFF_AQK + (x * 64 + l) * 16);
+      fal[x] = load_frag(blk + OFF_AQK + ((AQK_FRAGS + x) * 64 + l) * 16);
     }
 #pragma unroll
-    for (int tb = 0; tb < 8; tb += 4) {
-      bf16x8 fk[2][4];
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
+      for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          fk[s2][t] = load_frag(blk + OFF_KGT + (((tb + t) * 2 + s2) * 64 + l) * 16);
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2)
-            S[tb + t][q2] = mfma_bf16(fk[s2][t], vb[s2][q2], S[tb + t][q2]);
-    }
+        for (int q2 = 0; q2 < 2; ++q2) S[t][q2] = mfma_bf16(fk[s2][t], vb[s2][q2], S[t][q2]);
 
     // o^T += v_new^T Aqk^T   (Aqk in hi + lo bf16)
 #pragma unroll
-    for (int x = 0; x < AQK_FRAGS; ++x) {
-      const bf16x8 fah = load_frag(blk + OFF_AQK + (x * 64 + l) * 16);
-      const bf16x8 fal = load_frag(blk + OFF_AQK + ((AQK_FRAGS + x) * 64 + l) * 16);
+    for (int x = 0; x < AQK_FRAGS; ++x)
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
-        ot[LT_MT[x]][q2] = mfma_bf16(vb[LT_S[x]][q2], fah, ot[LT_MT[x]][q2]);
-        ot[LT_MT[x]][q2] = mfma_bf16(vb[LT_S[x]][q2], fal, ot[LT_MT[x]][q2]);
+        ot[LT_MT[x]][q2] = mfma_bf16(vb[LT_S[x]][q2], fah[x], ot[LT_MT[x]][q2]);
+        ot[LT_MT[x]][q2] = mfma_bf16(vb[LT_S[x]][q2], fal[x], ot[LT_MT[x]][q2]);
       }
-    }
 
     // o^T of this chunk as bf16 (nearest even), stored at the next chunk
 #pragma unroll
