@@ -6,6 +6,7 @@ Usage: python -m chunked_kda_prefill_amd.build  (or __graft_entry__.build()).
 from __future__ import annotations
 
 import glob
+import hashlib
 import os
 import subprocess
 import sys
@@ -33,6 +34,20 @@ HIPCC_FLAGS = [
 
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def source_hash() -> str:
+    """Short sha256 over every file the library is built from (sources,
+    headers, the public header and this file's flags).  Counter readings
+    taken for one build are only valid while this value is unchanged."""
+    files = sorted(glob.glob(os.path.join(CSRC, "*"))) + [
+        os.path.join(ROOT, "include", "kda.h"), os.path.abspath(__file__)]
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def build(verbose: bool = False) -> str:

@@ -1,6 +1,7 @@
 // Intra-chunk kernel: gate cumsum + strip-GEMMs + (I+L)^-1 + WY factors.
 //
-// One workgroup (8 waves) per (chunk, head).  With G the chunk-local
+// Each (chunk, head) unit is handled by one 8-wave workgroup (persistent: a
+// workgroup walks several units, see intra_kernel).  With G the chunk-local
 // inclusive cumsum of g, Gamma = exp(G), rows i, j of the chunk, and the
 // padding convention q = k = v = 0, g = 0, beta = 0 past a partial chunk's
 // end (so every quantity below is exactly zero or exactly carried there):
