@@ -83,32 +83,43 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t *__restr
 }
 
 // Standalone chunk-local cumsum: one workgroup per (chunk slot, head), with
-// the intra-chunk kernel's thread count so the summation order is the same.
-constexpr int CS_GLD = 132;
-
-__global__ __launch_bounds__(INTRA_THREADS) void gate_cumsum_kernel(const float *__restrict__ g,
-                                                          const int32_t *__restrict__ chunk_first,
-                                                          const int4 *__restrict__ chunk_info,
-                                                          int32_t N, int32_t H,
-                                                          float *__restrict__ Gout) {
-  __shared__ __align__(16) float G[BT][CS_GLD];
-  __shared__ __align__(16) float tot[INTRA_THREADS / 32][DK];
+// the intra-chunk kernel's chunk layout and summation order (kda_cumsum.h):
+// a DPP scan down each 16-row subblock, plus the running total of the
+// subblocks before it.
+__global__ __launch_bounds__(CHUNK_THREADS) void gate_cumsum_kernel(const float *__restrict__ g,
+                                                                    const int32_t *__restrict__ chunk_first,
+                                                                    const int4 *__restrict__ chunk_info,
+                                                                    int32_t N, int32_t H,
+                                                                    float *__restrict__ Gout) {
+  __shared__ __align__(16) float tot[CHUNK_WAVES * DK];
   const int64_t c = blockIdx.x / H;
   const int h = blockIdx.x % H;
   if (c >= chunk_first[N]) return;
   const int4 info = chunk_info[c];
   const int64_t t0 = info.x;
   const int n = info.y;
-  chunk_gate_cumsum<INTRA_THREADS>(g, t0, n, H, h, &G[0][0],
-                         [](int row, int ch) { return row * CS_GLD + ch; }, &tot[0][0]);
-  __syncthreads();
-  // write back rows < n: 32 lanes per row, 16 bytes each
   const int tid = threadIdx.x;
-  for (int idx = tid; idx < BT * 32; idx += INTRA_THREADS) {
-    const int i = idx >> 5, c4 = idx & 31;
-    if (i < n) {
-      *reinterpret_cast<float4 *>(Gout + ((t0 + i) * (int64_t)H + h) * DK + c4 * 4) =
-          *reinterpret_cast<const float4 *>(&G[i][c4 * 4]);
+  const int w = tid >> 6, nn = tid & 15, grp = (tid >> 4) & 3;
+  const int row = SB * w + nn;
+  float4 x[8];
+  gate_slots_load(g, t0, n, H, h, row, grp, x);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = subblock_scan(x[j]);
+  if (nn == SB - 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<float4 *>(&tot[w * DK + slot_ch(j, grp)]) = x[j];
+  }
+  __syncthreads();
+  if (row < n) {
+    float *out = Gout + ((t0 + row) * (int64_t)H + h) * DK;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int ch = slot_ch(j, grp);
+      const float4 y = make_float4(subblock_carry(tot, w, ch) + x[j].x,
+                                   subblock_carry(tot, w, ch + 1) + x[j].y,
+                                   subblock_carry(tot, w, ch + 2) + x[j].z,
+                                   subblock_carry(tot, w, ch + 3) + x[j].w);
+      *reinterpret_cast<float4 *>(out + ch) = y;
     }
   }
 }
@@ -124,7 +135,7 @@ hipError_t launch_chunk_table(const int32_t *cu, int64_t T, int32_t N, int64_t n
 hipError_t launch_gate_cumsum(const float *g, const int32_t *chunk_first, const int4 *chunk_info,
                               int64_t nc_max, int32_t N, int32_t H, float *G, hipStream_t stream) {
   if (nc_max <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gate_cumsum_kernel, dim3((unsigned)(nc_max * H)), dim3(INTRA_THREADS), 0,
+  hipLaunchKernelGGL(gate_cumsum_kernel, dim3((unsigned)(nc_max * H)), dim3(CHUNK_THREADS), 0,
                      stream, g,
                      chunk_first, chunk_info, N, H, G);
   return hipGetLastError();

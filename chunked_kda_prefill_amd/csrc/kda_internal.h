@@ -28,7 +28,6 @@ constexpr int DV = 128;
 constexpr int BT = 64;
 constexpr int SB = 16;
 constexpr int SB_REF = 7;  // subblock reference row (its midpoint)
-constexpr int INTRA_THREADS = 512;  // threads of the intra-chunk (and cumsum) workgroups
 
 typedef __bf16 bf16_t;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
