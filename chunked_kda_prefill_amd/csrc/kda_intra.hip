@@ -76,9 +76,22 @@ __device__ constexpr int OFF_B[6] = {0, 0, 1, 0, 1, 2};
 __device__ __forceinline__ int pair_idx(int a, int b) { return a * (a - 1) / 2 + b; }
 
 // The six (token tile, token slab) pairs of a 64 x 64 lower-triangular
-// operand that hold any j <= i; index = AQK_IDX(mt, s).
-__device__ constexpr int LT_MT[6] = {0, 1, 2, 2, 3, 3};
-__device__ constexpr int LT_S[6] = {0, 0, 0, 1, 0, 1};
+// operand that hold any j <= i; index x = AQK_IDX(mt, s): mt = 0,1,2,2,3,3
+// and s = 0,0,0,1,0,1 (computed, not table-driven, for runtime x).
+__device__ __forceinline__ int lt_mt(int x) { return (0x332210 >> (4 * x)) & 0xF; }
+__device__ __forceinline__ int lt_s(int x) { return (0x101000 >> (4 * x)) & 0xF; }
+
+// The chunk table is read-only while these kernels run: reading it through
+// the constant address space lets the compiler use scalar loads, which do
+// not wait on the kernel's own vector stores.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int4 chunk_record(const int4 *info, int64_t c) {
+  const i32x4 v = ((const __attribute__((address_space(4))) i32x4 *)(uintptr_t)info)[c];
+  return make_int4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ int32_t chunk_count(const int32_t *chunk_first, int N) {
+  return ((const __attribute__((address_space(4))) int32_t *)(uintptr_t)chunk_first)[N];
+}
 
 struct __align__(16) IntraSmem {
   // k~ (fp32 [64][128]) for the strips; then the kg and K*Gamma bf16 tiles
@@ -111,6 +124,14 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 }
 
 __device__ __forceinline__ f32x4 as_f32x4(float4 v) { return f32x4{v.x, v.y, v.z, v.w}; }
+
+// Materialises x in registers at this point, so the compiler cannot sink the
+// computation of a packed value to its far-away use (which would keep its
+// wider fp32 inputs alive in between).
+template <typename T>
+__device__ __forceinline__ void pin(T &x) {
+  asm volatile("" : "+v"(x));
+}
 
 // 16 x 16 x 16 fp32 product from C-layout registers: At holds A^T and B holds
 // B (lane (nn, grp), element r = row 4grp + r, column nn); k runs over
@@ -177,8 +198,10 @@ __device__ __forceinline__ void load_v(const IntraArgs &a, int64_t t0, int n, in
   }
 }
 
-// One (chunk, head) unit.
-__device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, int64_t u) {
+// One (chunk, head) unit whose inputs are already in `nxt` (loads issued).
+// After the unit's own inputs are consumed, `nxt` receives the next unit's.
+__device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, int64_t u,
+                                           int64_t units, UnitInputs &nxt) {
   // threadIdx.x through an opaque move, so that address arithmetic derived
   // from it stays inside the unit loop instead of being hoisted out of it
   int tid;
@@ -187,8 +210,11 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   const int row = SB * w + nn;
   const int64_t c = u / a.H;
   const int h = (int)(u % a.H);
-  UnitInputs in;
-  load_unit(a, a.chunk_info[c], h, row, grp, in);
+  // the next unit's chunk record, fetched now so that its data loads can be
+  // issued later without waiting on it
+  const int64_t un = u + gridDim.x;
+  const int4 info_next = chunk_record(a.chunk_info, (un < units ? un : u) / a.H);
+  UnitInputs in = nxt;
   const int n = in.n;
   uint8_t *blk = a.blocks + ((int64_t)h * a.nc_max + c) * BLOCK_BYTES;
   float *rt = sm.tt;  // [0, 4 DK): reference rows; [4 DK, 8 DK): subblock totals
@@ -277,9 +303,14 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
       }
       kgm[j] = pack4(kmv[0], kmv[1], kmv[2], kmv[3]);
       kgb[j] = pack4(kgv[0], kgv[1], kgv[2], kgv[3]);
+      pin(kgm[j]);
+      pin(kgb[j]);
       *reinterpret_cast<float4 *>(&sm.x[sw_f32(row, ch)]) = make_float4(ktv[0], ktv[1], ktv[2], ktv[3]);
     }
     store_bf16x8(blk + OFF_QG + ((w * 4 + s) * 64 + l) * 16, f);
+    pin(qh[s]);
+    pin(ql[s]);
+    pin(kh[s]);
     accA = mfma_bf16(kth, qh[s], accA);
     accA = mfma_bf16(kth, ql[s], accA);
     accA = mfma_bf16(ktl, qh[s], accA);
@@ -293,28 +324,40 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
     *reinterpret_cast<float2 *>(blk + OFF_GAM + 8 * l) = gv;
   }
 
-  const float4 bvec = *reinterpret_cast<const float4 *>(&sm.beta[SB * w + 4 * grp]);
-  auto strip_out = [&](int b, const f32x4 &accA, const f32x4 &accL, f32x4 &lv) {
+  // Epilogue of strip block (ba, bb): Aqk^T half to the block, L (times
+  // beta_i) to LDS; returns the L values the lane holds.
+  auto strip_out = [&](int ba, int bb, const f32x4 &accA, const f32x4 &accL, f32x4 &lv) {
     bf16x4 ah, al;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool keep = (w > b) || (4 * grp + r <= nn);
+      const bool keep = (ba > bb) || (4 * grp + r <= nn);
       split_bf16(keep ? accA[r] * a.scale : 0.f, ah, al, r);
     }
-    const int idx = AQK_IDX(w, b >> 1), half = b & 1;
+    const int idx = AQK_IDX(ba, bb >> 1), half = bb & 1;
     store_bf16x4(blk + OFF_AQK + (idx * 64 + l) * 16 + half * 8, ah);
     store_bf16x4(blk + OFF_AQK + ((AQK_FRAGS + idx) * 64 + l) * 16 + half * 8, al);
-    const f32x4 bv = as_f32x4(bvec);
+    const f32x4 bv = as_f32x4(*reinterpret_cast<const float4 *>(&sm.beta[SB * ba + 4 * grp]));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int il = 4 * grp + r;
-      const bool keep = (w > b) || (nn < il);
+      const bool keep = (ba > bb) || (nn < il);
       lv[r] = keep ? accL[r] * bv[r] : 0.f;
-      sm.lt[sw_lt(SB * w + il, SB * b + nn)] = lv[r];
+      sm.lt[sw_lt(SB * ba + il, SB * bb + nn)] = lv[r];
     }
   };
+  // Row-side fragments of subblock 3, for the waves that take two of its
+  // off-diagonal blocks; they go where T will be (past the cumsum rows).
+  bf16x8 *rowf = reinterpret_cast<bf16x8 *>(sm.tt + 8 * DK);
+  if (w == 3) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      rowf[(s * 3 + 0) * 64 + l] = qh[s];
+      rowf[(s * 3 + 1) * 64 + l] = ql[s];
+      rowf[(s * 3 + 2) * 64 + l] = kh[s];
+    }
+  }
   f32x4 Ld;  // L_ww (masked, beta-scaled) for the inverse
-  strip_out(w, accA, accL, Ld);
+  strip_out(w, w, accA, accL, Ld);
   if ((w & 1) == 0) {
     // the other half of the diagonal slab lies above the diagonal
     const bf16x4 z = {(bf16_t)0.f, (bf16_t)0.f, (bf16_t)0.f, (bf16_t)0.f};
@@ -324,14 +367,17 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   }
   __syncthreads();
 
-  // ---- off-diagonal strip blocks (w, b), b < w: k~_b from LDS times C_wb
-  for (int b = 0; b < w; ++b) {
-    const float *cab = sm.tab[TAB_C + pair_idx(w, b)];
-    const int j = SB * b + nn;
-    f32x4 accA = zero4(), accL = zero4();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 bh, bl;
+  // ---- the unit's q, k, g are consumed: start the next unit's loads ----
+  if (un < units) load_unit(a, info_next, (int)(un % a.H), row, grp, nxt);
+
+  // ---- off-diagonal strip blocks, two at most per wave:
+  //   wave 0: (3,0)   wave 1: (1,0) (3,1)   wave 2: (2,0) (2,1)   wave 3: (3,2)
+  // The column side is k~_b (LDS) times C_ab; the row side is the wave's own
+  // registers, or subblock 3's fragments from LDS for (3,0) and (3,1).
+  {
+    auto col_frag = [&](int ba, int bb, int s, bf16x8 &bh, bf16x8 &bl) {
+      const float *cab = sm.tab[TAB_C + pair_idx(ba, bb)];
+      const int j = SB * bb + nn;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int ch = slot_ch(2 * s + hh, grp);
@@ -342,13 +388,44 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
         split_bf16(kv.z * cv.z, bh, bl, 4 * hh + 2);
         split_bf16(kv.w * cv.w, bh, bl, 4 * hh + 3);
       }
-      accA = mfma_bf16(bh, qh[s], accA);
-      accA = mfma_bf16(bh, ql[s], accA);
-      accA = mfma_bf16(bl, qh[s], accA);
-      accL = mfma_bf16(kh[s], bh, accL);
+    };
+    auto step = [&](const bf16x8 &bh, const bf16x8 &bl, const bf16x8 &rqh, const bf16x8 &rql,
+                    const bf16x8 &rkh, f32x4 &accA, f32x4 &accL) {
+      accA = mfma_bf16(bh, rqh, accA);
+      accA = mfma_bf16(bh, rql, accA);
+      accA = mfma_bf16(bl, rqh, accA);
+      accL = mfma_bf16(rkh, bh, accL);
+    };
+    // first block: (ba0, bb0) with the row side in registers or LDS
+    const int ba0 = (w == 0) ? 3 : w, bb0 = (w == 3) ? 2 : 0;
+    const bool row0_lds = (w == 0);
+    // second block (waves 1, 2): (3,1) from LDS rows, or (2,1) own rows
+    const bool two = (w == 1) || (w == 2);
+    const int ba1 = (w == 1) ? 3 : 2, bb1 = 1;
+    const bool row1_lds = (w == 1);
+    f32x4 accA0 = zero4(), accL0 = zero4(), accA1 = zero4(), accL1 = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 bh, bl;
+      col_frag(ba0, bb0, s, bh, bl);
+      if (row0_lds)
+        step(bh, bl, rowf[(s * 3 + 0) * 64 + l], rowf[(s * 3 + 1) * 64 + l],
+             rowf[(s * 3 + 2) * 64 + l], accA0, accL0);
+      else
+        step(bh, bl, qh[s], ql[s], kh[s], accA0, accL0);
+      if (two) {
+        bf16x8 ch_, cl_;
+        col_frag(ba1, bb1, s, ch_, cl_);
+        if (row1_lds)
+          step(ch_, cl_, rowf[(s * 3 + 0) * 64 + l], rowf[(s * 3 + 1) * 64 + l],
+               rowf[(s * 3 + 2) * 64 + l], accA1, accL1);
+        else
+          step(ch_, cl_, qh[s], ql[s], kh[s], accA1, accL1);
+      }
     }
     f32x4 unused;
-    strip_out(b, accA, accL, unused);
+    strip_out(ba0, bb0, accA0, accL0, unused);
+    if (two) strip_out(ba1, bb1, accA1, accL1, unused);
   }
   __syncthreads();
 
@@ -460,8 +537,8 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   // L was; V rows into the tile where kg was ----
   bf16_t *tfr = reinterpret_cast<bf16_t *>(sm.lt);  // [hi: 6 x 64 lanes x 8][lo: 6 x 64 x 8]
   for (int x = w; x < 6; x += 4) {
-    const int i = SB * LT_MT[x] + nn;
-    const int j0 = 32 * LT_S[x] + 8 * grp;
+    const int i = SB * lt_mt(x) + nn;
+    const int j0 = 32 * lt_s(x) + 8 * grp;
     const float4 t0v = *reinterpret_cast<const float4 *>(&sm.tt[sw_lt(i, j0)]);
     const float4 t1v = *reinterpret_cast<const float4 *>(&sm.tt[sw_lt(i, j0 + 4)]);
     const float4 b0v = *reinterpret_cast<const float4 *>(&sm.beta[j0]);
@@ -549,18 +626,23 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
 }
 
 // Persistent: two workgroups per CU walk the (chunk, head) units with a
-// stride of the grid size.  While one waits on its loads or at a barrier,
-// the other computes.
+// stride of the grid size.  Each unit's inputs are loaded into registers
+// while the unit before it computes, and while one workgroup waits at a
+// barrier the other computes.
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void intra_kernel(
     IntraArgs a) {
   __shared__ IntraSmem sm;
   if (a.T <= 0) return;
-  int64_t nc = a.chunk_first[a.N];
+  int64_t nc = chunk_count(a.chunk_first, a.N);
   nc = nc < 0 ? 0 : (nc > a.nc_max ? a.nc_max : nc);
   const int64_t units = nc * a.H;
   int64_t u = blockIdx.x;
   if (u >= units) return;
-  for (; u < units; u += gridDim.x) intra_unit(a, sm, u);
+  const int tid = threadIdx.x;
+  UnitInputs nxt;
+  load_unit(a, chunk_record(a.chunk_info, u / a.H), (int)(u % a.H), SB * (tid >> 6) + (tid & 15),
+            (tid >> 4) & 3, nxt);
+  for (; u < units; u += gridDim.x) intra_unit(a, sm, u, units, nxt);
 }
 
 hipError_t launch_intra(const IntraArgs &a, hipStream_t stream) {
