@@ -51,7 +51,11 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 //          halves (hi fragments first).  Only the six (mt, s) fragments with
 //          any j <= i are stored, indexed by AQK_IDX.
 //   U    : U as the C-tile initialiser of v_new: [value tile nt 0..7][token
-//          tile mt 0..3] tiles of 64 lanes x 4 bf16 (C layout).
+//          tile mt 0..3] tiles of 64 lanes x 4 bf16 (C layout); lane (n, grp)
+//          element r holds U[16 mt + 4 grp + r][VCOL(nt, n)].  VCOL permutes
+//          the value columns inside each 32-column slice so that the
+//          recurrence's transposed output tiles give every lane 8
+//          consecutive columns of a token (one 16-byte store).
 //   GAM  : gamma = exp(G_last) per key channel, fp32 [128].
 // ---------------------------------------------------------------------------
 constexpr int FRAG_BYTES = 64 * 16;
@@ -65,6 +69,13 @@ constexpr int UTILE_BYTES = 64 * 8;
 constexpr int OFF_GAM = OFF_U + 32 * UTILE_BYTES;
 constexpr int BLOCK_BYTES = OFF_GAM + DK * 4;
 static_assert(BLOCK_BYTES % 256 == 0, "intermediate blocks stay 256-byte aligned");
+
+// Value column held by lane n of value tile nt in the recurrence's state,
+// v_new and U tiles: column x = n of the tile maps to
+// 32 (nt / 2) + 8 (x / 4) + 4 (nt % 2) + x % 4.
+__host__ __device__ constexpr int VCOL(int nt, int n) {
+  return 32 * (nt >> 1) + 8 * (n >> 2) + 4 * (nt & 1) + (n & 3);
+}
 
 // Aqk fragment (token tile mt, token slab s) -> storage index; valid for
 // s <= mt / 2, i.e. (0,0) (1,0) (2,0) (2,1) (3,0) (3,1).

@@ -510,11 +510,14 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   // Transposed LDS read of a row-major bf16 tile (ds_read_b64_tr_b16): within
   // each group of 16 lanes, lane j addresses row r0 + j/4, columns
   // c0 + 4 (j%4) .. +3, and lane i receives tile[r0 + 0..3][c0 + i].
-  auto tr4 = [&](const bf16_t *tile, int r0, int c0) -> bf16x4 {
-    const bf16_t *p = &tile[sw_bf16(r0 + (nn >> 2), c0 + 4 * (nn & 3))];
+  // tr4c: the same with lane j addressing columns c_lane .. c_lane + 3 (any
+  // 4-aligned start); lane i then receives column c_lane(i / 4) + i % 4.
+  auto tr4c = [&](const bf16_t *tile, int r0, int c_lane) -> bf16x4 {
+    const bf16_t *p = &tile[sw_bf16(r0 + (nn >> 2), c_lane)];
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
         (__attribute__((address_space(3))) bf16x4 *)(p));
   };
+  auto tr4 = [&](const bf16_t *tile, int r0, int c0) -> bf16x4 { return tr4c(tile, r0, c0 + 4 * (nn & 3)); };
 
   // ---- kg^T fragments: wave w writes key tiles 2w and 2w+1; slot e of
   // lane (nn, grp) holds kg[P(s, grp, e)][16 mtc + nn] ----
@@ -560,15 +563,18 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   auto th = [&](int x) { return *reinterpret_cast<const bf16x8 *>(&tfr[(x * 64 + l) * 8]); };
   auto tl = [&](int x) { return *reinterpret_cast<const bf16x8 *>(&tfr[((6 + x) * 64 + l) * 8]); };
 
-  // ---- U = T' V: wave w writes value tiles 2w and 2w+1 (C layout) ----
+  // ---- U = T' V: wave w writes value tiles 2w and 2w+1 (C layout, value
+  // columns VCOL(nt, nn): the tr-read lanes j address column VCOL(nt, 4 (j % 4))
+  // so that lane i receives column VCOL(nt, i)) ----
 #pragma unroll
   for (int q2 = 0; q2 < 2; ++q2) {
     const int nt = 2 * w + q2;
+    const int vc = VCOL(nt, 4 * (nn & 3));
     bf16x8 vb[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const bf16x4 lo4 = tr4(vt, 32 * s + 8 * grp, 16 * nt);
-      const bf16x4 hi4 = tr4(vt, 32 * s + 8 * grp + 4, 16 * nt);
+      const bf16x4 lo4 = tr4c(vt, 32 * s + 8 * grp, vc);
+      const bf16x4 hi4 = tr4c(vt, 32 * s + 8 * grp + 4, vc);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         vb[s][e] = lo4[e];

@@ -21,24 +21,27 @@ namespace {
 __device__ constexpr int LT_MT[6] = {0, 1, 2, 2, 3, 3};
 __device__ constexpr int LT_S[6] = {0, 0, 0, 1, 0, 1};
 
+// The chunk table is read-only while this kernel runs: reading it through
+// the constant address space gives scalar loads.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int4 chunk_record(const int4 *info, int64_t c) {
+  const i32x4 v = ((const __attribute__((address_space(4))) i32x4 *)(uintptr_t)info)[c];
+  return make_int4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ bf16x8 load_frag(const uint8_t *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }
 
-// o rows of one chunk: lane holds token 16 mt + nn and value columns
-// 16 (2w + q2) + 4 grp .. + 3, i.e. one 8-byte store per (mt, q2).
-__device__ __forceinline__ void store_o(const RecurArgs &a, int h, int w, int nn, int grp,
-                                        int64_t t0, int n, const bf16x4 (&ov)[4][2]) {
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int row = 16 * mt + nn;
-    if (row < n) {
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
-        *reinterpret_cast<bf16x4 *>(a.o + ((t0 + row) * a.H + h) * DV + 16 * (2 * w + q2) +
-                                    4 * grp) = ov[mt][q2];
-    }
-  }
+// o rows of token tile mt of one chunk: the transposed output tiles of value
+// tiles 2w and 2w+1 give lane (nn, grp) token 16 mt + nn and the value
+// columns VCOL(2w + q2, 4 grp + r) = 32 w + 8 grp + 4 q2 + r, i.e. 8
+// consecutive columns: one 16-byte store.
+__device__ __forceinline__ void store_o_tile(const RecurArgs &a, int h, int w, int nn, int grp,
+                                             int64_t t0, int n, int mt, const bf16x8 &ov) {
+  const int row = 16 * mt + nn;
+  if (row < n)
+    *reinterpret_cast<bf16x8 *>(a.o + ((t0 + row) * a.H + h) * DV + 32 * w + 8 * grp) = ov;
 }
 
 }  // namespace
@@ -55,10 +58,27 @@ constexpr int DMA_FULL = BLOCK_BYTES / DMA_ROUND;          // 19 full rounds
 constexpr int DMA_TAIL = BLOCK_BYTES - DMA_FULL * DMA_ROUND;  // 512 bytes
 static_assert(DMA_TAIL % 16 == 0 && DMA_TAIL <= 64 * 16, "tail fits one wave");
 
+// One global_load_lds_dwordx4: 16 bytes per lane from src into LDS at
+// lds_wave_base + 16 * lane.  Written as inline assembly so that the
+// compiler does not treat it as an LDS store it must wait for before every
+// later LDS read (it cannot tell the two block buffers apart); the kernel
+// waits for these copies itself, at the top of each chunk.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
 __device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(
-      (const __attribute__((address_space(1))) void *)src,
-      (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const uint8_t *src, uint8_t *lds_wave_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(base)
+               : "memory", "m0");
 }
 
 // Copy one intermediate block into an LDS buffer: lane l of wave w copies
@@ -74,6 +94,29 @@ __device__ __forceinline__ void copy_block_part(const uint8_t *src, uint8_t *dst
   if (part == 3 && w == 0 && l < DMA_TAIL / 16)
     dma16(src + DMA_FULL * DMA_ROUND + l * 16, dst + DMA_FULL * DMA_ROUND);
 }
+// Touch the block two chunks ahead, one dword per 128-byte line, so that its
+// copy a chunk later hits L2 instead of HBM.  The loaded dwords land in a
+// junk LDS word per lane (global_load_lds: no registers, so nothing waits on
+// them until the explicit wait at the next chunk, which leaves exactly these
+// TOUCH_LOADS instructions in flight).
+constexpr int LINE_BYTES = 128;
+constexpr int TOUCH_LINES = (BLOCK_BYTES + LINE_BYTES - 1) / LINE_BYTES;  // 612
+constexpr int TOUCH_LOADS = (TOUCH_LINES + REC_THREADS - 1) / REC_THREADS;  // 3
+__device__ __forceinline__ void touch_block(const uint8_t *src, uint8_t *junk_wave, int tid) {
+#pragma unroll
+  for (int k = 0; k < TOUCH_LOADS; ++k) {
+    int line = tid + REC_THREADS * k;
+    line = line < TOUCH_LINES ? line : 0;
+    dma4(src + line * LINE_BYTES, junk_wave);
+  }
+}
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8]):
+// all LDS/scalar work done and all vector memory done except the last
+// TOUCH_LOADS (or none) issued
+constexpr int WAIT_ALL_BUT_TOUCH = TOUCH_LOADS | (7 << 4);
+constexpr int WAIT_ALL = 0 | (7 << 4);
+static_assert(TOUCH_LOADS < 16, "fits the low vmcnt field");
+
 __device__ __forceinline__ void copy_block(const uint8_t *src, uint8_t *dst, int w, int l) {
 #pragma unroll
   for (int part = 0; part < 4; ++part) copy_block_part(src, dst, w, l, part);
@@ -81,6 +124,7 @@ __device__ __forceinline__ void copy_block(const uint8_t *src, uint8_t *dst, int
 
 __global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
   __shared__ __align__(16) uint8_t lds[2][BLOCK_BYTES];
+  __shared__ __align__(16) uint8_t junk[REC_THREADS / 64][64 * 4];
   const int64_t chain = blockIdx.x;
   if (chain >= (int64_t)a.N * a.H) return;
   const int s = (int)(chain / a.H), h = (int)(chain % a.H);
@@ -104,7 +148,7 @@ __global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * t + 4 * grp + r;
-        const int col = 16 * (2 * w + q2) + nn;
+        const int col = VCOL(2 * w + q2, nn);
         S[t][q2][r] = a.h0 ? a.h0[st_base + row * DV + col] : 0.f;
       }
 
@@ -113,21 +157,25 @@ __global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
   // o of chunk c is stored at the start of chunk c+1, right after the next
   // copy is issued, so that the store latency overlaps a whole chunk of work
   // instead of the wait for that copy
-  bf16x4 o_pend[4][2];
+  bf16x8 o_pend[4];
   int64_t o_t0 = 0;
   int o_n = 0;
 
+  bool touched = false;  // loads of touch_block still in flight
   for (int64_t c = c_beg; c < c_end; ++c) {
     const int cur = (int)((c - c_beg) & 1);
     // this thread's copies (and earlier stores) are done; after the barrier
     // every thread's are, and nobody still reads the other buffer
-    __builtin_amdgcn_s_waitcnt(0);
+    if (touched)
+      __builtin_amdgcn_s_waitcnt(WAIT_ALL_BUT_TOUCH);
+    else
+      __builtin_amdgcn_s_waitcnt(WAIT_ALL);
     __syncthreads();
     const bool more = c + 1 < c_end;
     const uint8_t *next_src = chain_blocks + (c + 1) * BLOCK_BYTES;
     uint8_t *next_dst = lds[cur ^ 1];
     const uint8_t *blk = lds[cur];
-    const int4 info = a.chunk_info[c];
+    const int4 info = chunk_record(a.chunk_info, c);
     const int64_t t0 = info.x < 0 ? 0 : (info.x > a.T ? a.T : info.x);
     const int n = (int)(info.y < 0 ? 0 : (info.y > a.T - t0 ? a.T - t0 : info.y));
 
@@ -182,8 +230,12 @@ __global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       // one quarter of the next chunk's copy (and, first, last chunk's o)
-      if (s4 == 0 && c > c_beg) store_o(a, h, w, nn, grp, o_t0, o_n, o_pend);
+      if (c > c_beg) store_o_tile(a, h, w, nn, grp, o_t0, o_n, s4, o_pend[s4]);
       if (more) copy_block_part(next_src, next_dst, w, l, s4);
+      if (s4 == 3) {
+        touched = c + 2 < c_end;
+        if (touched) touch_block(chain_blocks + (c + 2) * BLOCK_BYTES, junk[w], tid);
+      }
       bf16x8 nw[4], nq[4];
       if (s4 < 3) {
 #pragma unroll
@@ -252,11 +304,16 @@ __global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o_pend[mt][q2][r] = (bf16_t)ot[mt][q2][r];
+        for (int r = 0; r < 4; ++r) o_pend[mt][4 * q2 + r] = (bf16_t)ot[mt][q2][r];
     o_t0 = t0;
     o_n = n;
   }
-  if (c_end > c_beg) store_o(a, h, w, nn, grp, o_t0, o_n, o_pend);
+  if (c_end > c_beg) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) store_o_tile(a, h, w, nn, grp, o_t0, o_n, mt, o_pend[mt]);
+  }
+  // no load may still be writing LDS when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(WAIT_ALL);
 
   if (a.hT) {
 #pragma unroll
@@ -266,7 +323,7 @@ __global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * t + 4 * grp + r;
-          const int col = 16 * (2 * w + q2) + nn;
+          const int col = VCOL(2 * w + q2, nn);
           a.hT[st_base + row * DV + col] = S[t][q2][r];
         }
   }

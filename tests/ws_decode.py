@@ -18,6 +18,11 @@ def _bf16(raw):
     return (raw.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def _vcol(nt, n):
+    """Value column of lane n in value tile nt (kda_internal.h VCOL)."""
+    return 32 * (nt >> 1) + 8 * (n >> 2) + 4 * (nt & 1) + (n & 3)
+
+
 def _perm_index(s, grp, e):
     return 32 * s + 16 * (e >> 2) + 4 * grp + (e & 3)
 
@@ -64,6 +69,6 @@ def decode_block(raw: np.ndarray) -> dict:
             for l in range(64):
                 n, grp = l & 15, l >> 4
                 for r in range(4):
-                    U[16 * mt + 4 * grp + r, 16 * nt + n] = t[l, r]
+                    U[16 * mt + 4 * grp + r, _vcol(nt, n)] = t[l, r]
     gam = raw[OFF_GAM:OFF_GAM + 512].view(np.float32).astype(np.float64)
     return {"W": W, "qg": QG, "kg": KG, "Aqk": AQK, "U": U, "gamma": gam}
