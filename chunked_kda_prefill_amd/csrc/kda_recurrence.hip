@@ -6,11 +6,15 @@
 //     v_new = U - W h
 //     o     = qg h + Aqk v_new              (reads the entry state h)
 //     h     = Diag(gamma) h + kg^T v_new
-// The 128 value columns of the state are independent, so each of the 4 waves
-// of a chain's workgroup keeps a [128, 32] fp32 slice of the state in 16 MFMA
-// C tiles for the whole sequence; the state and v_new are fed back to the
-// MFMAs as B operands straight from their C tiles (bf16), in the permuted k
-// order the intra-chunk kernel wrote its A fragments in.
+// The 128 value columns of the state are independent.  A chain is split
+// over PARTS workgroups, each owning TILES value tiles of 16 columns (wave w
+// owns TPW of them) and keeping its [128, 16 TPW] fp32 slice of the state in
+// MFMA C tiles for the whole sequence; the state and v_new are fed back to
+// the MFMAs as B operands straight from their C tiles (bf16), in the
+// permuted k order the intra-chunk kernel wrote its A fragments in.  Fewer
+// columns per wave shorten the serial per-chunk work of every wave, which
+// is what bounds a chain; the split is picked at launch so that the
+// workgroups still fit the device once each.
 #include "kda_internal.h"
 #include "kda_launch.h"
 
@@ -18,8 +22,10 @@ namespace kda {
 
 namespace {
 
-__device__ constexpr int LT_MT[6] = {0, 1, 2, 2, 3, 3};
-__device__ constexpr int LT_S[6] = {0, 0, 0, 1, 0, 1};
+// The six (token tile, token slab) fragments of a 64 x 64 lower-triangular
+// operand: index x -> (mt, s) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1).
+constexpr int lt_mt(int x) { return x < 2 ? x : (x < 4 ? 2 : 3); }
+constexpr int lt_s(int x) { return (x == 3 || x == 5) ? 1 : 0; }
 
 // The chunk table is read-only while this kernel runs: reading it through
 // the constant address space gives scalar loads.
@@ -28,35 +34,13 @@ __device__ __forceinline__ int4 chunk_record(const int4 *info, int64_t c) {
   const i32x4 v = ((const __attribute__((address_space(4))) i32x4 *)(uintptr_t)info)[c];
   return make_int4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ int32_t chunk_first_of(const int32_t *chunk_first, int64_t s) {
+  return ((const __attribute__((address_space(4))) int32_t *)(uintptr_t)chunk_first)[s];
+}
 
 __device__ __forceinline__ bf16x8 load_frag(const uint8_t *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }
-
-// o rows of token tile mt of one chunk: the transposed output tiles of value
-// tiles 2w and 2w+1 give lane (nn, grp) token 16 mt + nn and the value
-// columns VCOL(2w + q2, 4 grp + r) = 32 w + 8 grp + 4 q2 + r, i.e. 8
-// consecutive columns: one 16-byte store.
-__device__ __forceinline__ void store_o_tile(const RecurArgs &a, int h, int w, int nn, int grp,
-                                             int64_t t0, int n, int mt, const bf16x8 &ov) {
-  const int row = 16 * mt + nn;
-  if (row < n)
-    *reinterpret_cast<bf16x8 *>(a.o + ((t0 + row) * a.H + h) * DV + 32 * w + 8 * grp) = ov;
-}
-
-}  // namespace
-
-// One workgroup of 4 waves per (sequence, head) chain; wave w owns value
-// tiles 2w and 2w+1 (32 columns) of the state.  The chain's intermediate
-// blocks stream through two LDS buffers: while the waves compute chunk c from
-// one buffer, chunk c+1's block is copied global -> LDS into the other by
-// global_load_lds_dwordx4 (no register staging), so the four waves share one
-// copy of the fragments and the copy latency hides behind the MFMAs.
-constexpr int REC_THREADS = 256;
-constexpr int DMA_ROUND = REC_THREADS * 16;               // bytes per copy round
-constexpr int DMA_FULL = BLOCK_BYTES / DMA_ROUND;          // 19 full rounds
-constexpr int DMA_TAIL = BLOCK_BYTES - DMA_FULL * DMA_ROUND;  // 512 bytes
-static_assert(DMA_TAIL % 16 == 0 && DMA_TAIL <= 64 * 16, "tail fits one wave");
 
 // One global_load_lds_dwordx4: 16 bytes per lane from src into LDS at
 // lds_wave_base + 16 * lane.  Written as inline assembly so that the
@@ -73,6 +57,7 @@ __device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *lds_wave_base
                : "v"(src), "s"(base)
                : "memory", "m0");
 }
+
 __device__ __forceinline__ void dma4(const uint8_t *src, uint8_t *lds_wave_base) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
@@ -81,99 +66,194 @@ __device__ __forceinline__ void dma4(const uint8_t *src, uint8_t *lds_wave_base)
                : "memory", "m0");
 }
 
-// Copy one intermediate block into an LDS buffer: lane l of wave w copies
-// the 16 bytes at round * 4096 + w * 1024 + l * 16.  The copy is issued in
-// four parts spread over a chunk's MFMA work, so that the wave never stalls
-// on a burst of memory instructions.
-constexpr int DMA_PART = (DMA_FULL + 3) / 4;
-__device__ __forceinline__ void copy_block_part(const uint8_t *src, uint8_t *dst, int w, int l,
-                                                int part) {
-#pragma unroll
-  for (int r = part * DMA_PART; r < (part + 1) * DMA_PART && r < DMA_FULL; ++r)
-    dma16(src + r * DMA_ROUND + w * 1024 + l * 16, dst + r * DMA_ROUND + w * 1024);
-  if (part == 3 && w == 0 && l < DMA_TAIL / 16)
-    dma16(src + DMA_FULL * DMA_ROUND + l * 16, dst + DMA_FULL * DMA_ROUND);
+constexpr int ROUND = 1024;                  // one wave's copy: 64 lanes x 16 bytes
+constexpr int SHARED_ROUNDS = OFF_U / ROUND;  // -W, qg, kg^T, Aqk: every part needs them
+static_assert(OFF_U % ROUND == 0, "shared fragments are whole rounds");
+static_assert(OFF_GAM + DK * 4 == BLOCK_BYTES, "gamma ends the block");
+
+// NC compute waves (TPW value tiles each) and NCP copy waves per workgroup.
+template <int NC, int NCP, int TPW>
+struct RecCfg {
+  static constexpr int THREADS = 64 * (NC + NCP);
+  static constexpr int NCW = NC;              // compute waves
+  static constexpr int TILES = NC * TPW;      // value tiles per workgroup
+  static constexpr int PARTS = 8 / TILES;     // workgroups per chain
+  static constexpr int U_ROUNDS = TILES * 4 * UTILE_BYTES / ROUND;
+  // shared fragments, this part's U tiles, and gamma (half a round)
+  static constexpr int ROUNDS = SHARED_ROUNDS + U_ROUNDS + 1;
+  static_assert(TILES * PARTS == 8, "parts cover the 128 value columns");
+};
+
+// Copy round k of part p's share of a block (same offsets in LDS as in the
+// block): shared rounds, then the part's U tiles, then gamma (lanes < 32).
+template <class C>
+__device__ __forceinline__ void copy_round(const uint8_t *src, uint8_t *dst, int k, int p, int l) {
+  int off;
+  if (k < SHARED_ROUNDS)
+    off = k * ROUND;
+  else if (k < SHARED_ROUNDS + C::U_ROUNDS)
+    off = OFF_U + (p * C::U_ROUNDS + (k - SHARED_ROUNDS)) * ROUND;
+  else
+    off = OFF_GAM;
+  if (k < C::ROUNDS - 1 || l < DK * 4 / 16) dma16(src + off + l * 16, dst + off);
 }
-// Touch the block two chunks ahead, one dword per 128-byte line, so that its
-// copy a chunk later hits L2 instead of HBM.  The loaded dwords land in a
-// junk LDS word per lane (global_load_lds: no registers, so nothing waits on
-// them until the explicit wait at the next chunk, which leaves exactly these
-// TOUCH_LOADS instructions in flight).
-constexpr int LINE_BYTES = 128;
-constexpr int TOUCH_LINES = (BLOCK_BYTES + LINE_BYTES - 1) / LINE_BYTES;  // 612
-constexpr int TOUCH_LOADS = (TOUCH_LINES + REC_THREADS - 1) / REC_THREADS;  // 3
-__device__ __forceinline__ void touch_block(const uint8_t *src, uint8_t *junk_wave, int tid) {
+
+// Without copy waves: compute wave w copies rounds w, w + NC, ..., a
+// quarter of them at each key slab of the chunk before.
+template <class C>
+__device__ __forceinline__ void copy_step(const uint8_t *src, uint8_t *dst, int w, int p, int l,
+                                          int step) {
+  constexpr int per_wave = (C::ROUNDS + C::NCW - 1) / C::NCW;
+  constexpr int per_step = (per_wave + 3) / 4;
 #pragma unroll
-  for (int k = 0; k < TOUCH_LOADS; ++k) {
-    int line = tid + REC_THREADS * k;
-    line = line < TOUCH_LINES ? line : 0;
-    dma4(src + line * LINE_BYTES, junk_wave);
+  for (int j = step * per_step; j < (step + 1) * per_step && j < per_wave; ++j) {
+    const int k = w + C::NCW * j;
+    if (k < C::ROUNDS) copy_round<C>(src, dst, k, p, l);
   }
 }
-// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8]):
-// all LDS/scalar work done and all vector memory done except the last
-// TOUCH_LOADS (or none) issued
-constexpr int WAIT_ALL_BUT_TOUCH = TOUCH_LOADS | (7 << 4);
-constexpr int WAIT_ALL = 0 | (7 << 4);
-static_assert(TOUCH_LOADS < 16, "fits the low vmcnt field");
 
-__device__ __forceinline__ void copy_block(const uint8_t *src, uint8_t *dst, int w, int l) {
+// Touch a whole block, one dword per 128-byte line, from the NCP copy waves
+// (loads land in a junk LDS word per lane), so that the copy a chunk later
+// hits L2.  Every lane issues TOUCH_LOADS loads, so the number in flight is
+// known to the explicit waits.
+constexpr int TOUCH_LINES = (BLOCK_BYTES + 127) / 128;  // 612
+template <int NCP>
+struct Touch {
+  static constexpr int LOADS = NCP > 0 ? (TOUCH_LINES + 64 * NCP - 1) / (64 * NCP) : 1;
+  static_assert(LOADS < 16, "fits the low vmcnt field");
+  // s_waitcnt immediates (vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8])
+  static constexpr int WAIT_ALL_BUT_TOUCH = LOADS | (7 << 4);
+};
+template <int NCP>
+__device__ __forceinline__ void touch_block(const uint8_t *src, uint8_t *junk_wave, int ct) {
 #pragma unroll
-  for (int part = 0; part < 4; ++part) copy_block_part(src, dst, w, l, part);
+  for (int k = 0; k < Touch<NCP>::LOADS; ++k) {
+    int line = ct + 64 * NCP * k;
+    line = line < TOUCH_LINES ? line : 0;
+    dma4(src + line * 128, junk_wave);
+  }
 }
 
-__global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
+// Copy wave cw's share of part p's block: rounds cw, cw + NCP, ...
+template <class C, int NCP>
+__device__ __forceinline__ void copy_share(const uint8_t *src, uint8_t *dst, int cw, int p, int l) {
+#pragma unroll
+  for (int k0 = 0; k0 < C::ROUNDS; k0 += NCP) {
+    const int k = k0 + cw;
+    if (k < C::ROUNDS) copy_round<C>(src, dst, k, p, l);
+  }
+}
+
+}  // namespace
+
+// Kernel: PARTS workgroups per chain, NC + NCP waves each.  The NC compute
+// waves never issue a copy: the NCP copy waves (on otherwise idle SIMDs)
+// stream chunk c+1's block into the other LDS buffer while the compute
+// waves work on chunk c, and both meet at one barrier per chunk.  Workgroups of one chain
+// get block indices congruent mod 8, so that (with the round-robin
+// workgroup-to-XCD dispatch) they run on one XCD and share its L2: a block is
+// read from HBM once and hit in L2 by the other parts.  The chain's
+// intermediate blocks stream through two LDS buffers: while the waves compute
+// chunk c from one buffer, chunk c+1's block is copied global -> LDS into
+// the other by global_load_lds_dwordx4 (no register staging).
+template <int NC, int NCP, int TPW>
+__global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a) {
+  using C = RecCfg<NC, NCP, TPW>;
   __shared__ __align__(16) uint8_t lds[2][BLOCK_BYTES];
-  __shared__ __align__(16) uint8_t junk[REC_THREADS / 64][64 * 4];
-  const int64_t chain = blockIdx.x;
+  __shared__ __align__(16) uint8_t junk[NCP > 0 ? NCP : 1][64 * 4];
+  const int b = blockIdx.x;
+  const int xcd = b & 7, i = b >> 3;
+  const int64_t chain = (int64_t)(i / C::PARTS) * 8 + xcd;
+  const int p = i % C::PARTS;
   if (chain >= (int64_t)a.N * a.H) return;
   const int s = (int)(chain / a.H), h = (int)(chain % a.H);
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, nn = l & 15, grp = l >> 4;
+  const int nt0 = p * C::TILES + w * TPW;  // a compute wave's first value tile
   // chunk range and token ranges are clamped so that a workspace that does
   // not hold a valid chunk table can never send this kernel out of bounds
   const int64_t nc_max = a.nc_max;
-  int64_t c_beg = a.chunk_first[s], c_end = a.chunk_first[s + 1];
+  int64_t c_beg = chunk_first_of(a.chunk_first, s), c_end = chunk_first_of(a.chunk_first, s + 1);
   c_beg = c_beg < 0 ? 0 : (c_beg > nc_max ? nc_max : c_beg);
   c_end = c_end < c_beg ? c_beg : (c_end > nc_max ? nc_max : c_end);
   const int64_t st_base = ((int64_t)s * a.H + h) * DK * DV;
   const uint8_t *chain_blocks = a.blocks + (int64_t)h * nc_max * BLOCK_BYTES;
 
-  // state slice: key tiles t = 0..7, value tiles 2w + q2
-  f32x4 S[8][2];
+  if (NCP > 0 && w >= NC) {
+    // ---- copy waves: chunk c+1's block while chunk c is computed ----
+    // The chain's first part also touches the block two chunks ahead (the
+    // parts share one L2), leaving those loads in flight across the wait.
+    const int cw = w - NC;
+    const bool toucher = (p == 0);
+    if (c_beg < c_end) copy_share<C, NCP>(chain_blocks + c_beg * BLOCK_BYTES, lds[0], cw, p, l);
+    if (toucher && c_beg + 1 < c_end)
+      touch_block<NCP>(chain_blocks + (c_beg + 1) * BLOCK_BYTES, junk[cw], cw * 64 + l);
+    bool touched = toucher && c_beg + 1 < c_end;
+    for (int64_t c = c_beg; c < c_end; ++c) {
+      if (touched)
+        __builtin_amdgcn_s_waitcnt(Touch<NCP>::WAIT_ALL_BUT_TOUCH);
+      else
+        __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (c + 1 < c_end)
+        copy_share<C, NCP>(chain_blocks + (c + 1) * BLOCK_BYTES, lds[(int)((c - c_beg) & 1) ^ 1], cw,
+                           p, l);
+      touched = toucher && c + 2 < c_end;
+      if (touched) touch_block<NCP>(chain_blocks + (c + 2) * BLOCK_BYTES, junk[cw], cw * 64 + l);
+    }
+    // no copy may still be writing LDS when the workgroup ends
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+
+  // ---- compute waves ----
+  // state slice: key tiles t = 0..7, value tiles nt0 + q
+  f32x4 S[8][TPW];
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2)
+    for (int q = 0; q < TPW; ++q)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * t + 4 * grp + r;
-        const int col = VCOL(2 * w + q2, nn);
-        S[t][q2][r] = a.h0 ? a.h0[st_base + row * DV + col] : 0.f;
+        const int col = VCOL(nt0 + q, nn);
+        S[t][q][r] = a.h0 ? a.h0[st_base + row * DV + col] : 0.f;
       }
 
-  if (c_beg < c_end) copy_block(chain_blocks + c_beg * BLOCK_BYTES, lds[0], w, l);
+  if (NCP == 0 && c_beg < c_end) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      copy_step<C>(chain_blocks + c_beg * BLOCK_BYTES, lds[0], w, p, l, st);
+  }
 
-  // o of chunk c is stored at the start of chunk c+1, right after the next
-  // copy is issued, so that the store latency overlaps a whole chunk of work
-  // instead of the wait for that copy
-  bf16x8 o_pend[4];
+  // o of chunk c is stored during chunk c+1, one token tile per key slab,
+  // so that the stores overlap a whole chunk of work.  With two value tiles
+  // per wave the lane holds 8 consecutive columns of a token (VCOL), else 4.
+  bf16x4 o_pend[4][TPW];
   int64_t o_t0 = 0;
   int o_n = 0;
+  auto store_o_tile = [&](int mt) {
+    const int row = 16 * mt + nn;
+    if (row < o_n) {
+      bf16_t *dst = reinterpret_cast<bf16_t *>(a.o) + ((o_t0 + row) * a.H + h) * DV +
+                    VCOL(nt0, 4 * grp);
+      if (TPW == 2) {
+        const bf16x8 v = {o_pend[mt][0][0], o_pend[mt][0][1], o_pend[mt][0][2], o_pend[mt][0][3],
+                          o_pend[mt][TPW - 1][0], o_pend[mt][TPW - 1][1], o_pend[mt][TPW - 1][2],
+                          o_pend[mt][TPW - 1][3]};
+        *reinterpret_cast<bf16x8 *>(dst) = v;
+      } else {
+        *reinterpret_cast<bf16x4 *>(dst) = o_pend[mt][0];
+      }
+    }
+  };
 
-  bool touched = false;  // loads of touch_block still in flight
   for (int64_t c = c_beg; c < c_end; ++c) {
     const int cur = (int)((c - c_beg) & 1);
-    // this thread's copies (and earlier stores) are done; after the barrier
-    // every thread's are, and nobody still reads the other buffer
-    if (touched)
-      __builtin_amdgcn_s_waitcnt(WAIT_ALL_BUT_TOUCH);
-    else
-      __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+    // after the barrier the copy waves' copies of this chunk are done, and
+    // nobody still reads the other buffer
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const bool more = c + 1 < c_end;
-    const uint8_t *next_src = chain_blocks + (c + 1) * BLOCK_BYTES;
-    uint8_t *next_dst = lds[cur ^ 1];
     const uint8_t *blk = lds[cur];
     const int4 info = chunk_record(a.chunk_info, c);
     const int64_t t0 = info.x < 0 ? 0 : (info.x > a.T ? a.T : info.x);
@@ -189,25 +269,25 @@ __global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
     }
 
     // entry state as bf16 MFMA operands (k slabs of 32 key rows)
-    bf16x8 hb[4][2];
+    bf16x8 hb[4][TPW];
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
+      for (int q = 0; q < TPW; ++q)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) hb[s4][q2][e] = (bf16_t)S[2 * s4 + (e >> 2)][q2][e & 3];
+        for (int e = 0; e < 8; ++e) hb[s4][q][e] = (bf16_t)S[2 * s4 + (e >> 2)][q][e & 3];
 
     // v_new starts from U (C layout: [token][value]); o^T from zero
-    f32x4 vn[4][2], ot[4][2];
+    f32x4 vn[4][TPW], ot[4][TPW];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
+      for (int q = 0; q < TPW; ++q) {
         const bf16x4 u = *reinterpret_cast<const bf16x4 *>(
-            blk + OFF_U + (((2 * w + q2) * 4 + mt) * 64 + l) * 8);
+            blk + OFF_U + (((nt0 + q) * 4 + mt) * 64 + l) * 8);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vn[mt][q2][r] = (float)u[r];
-        ot[mt][q2] = zero4();
+        for (int r = 0; r < 4; ++r) vn[mt][q][r] = (float)u[r];
+        ot[mt][q] = zero4();
       }
 
     // the state is no longer needed unscaled: apply Diag(gamma) now, while
@@ -216,26 +296,24 @@ __global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
     for (int t = 0; t < 8; ++t) {
       const float4 gm = *reinterpret_cast<const float4 *>(blk + OFF_GAM + (16 * t + 4 * grp) * 4);
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        S[t][q2][0] *= gm.x;
-        S[t][q2][1] *= gm.y;
-        S[t][q2][2] *= gm.z;
-        S[t][q2][3] *= gm.w;
+      for (int q = 0; q < TPW; ++q) {
+        S[t][q][0] *= gm.x;
+        S[t][q][1] *= gm.y;
+        S[t][q][2] *= gm.z;
+        S[t][q][3] *= gm.w;
       }
     }
 
     // v_new += (-W) h   and   o^T += h^T qg^T   (o is formed transposed so
-    // that each lane ends up with 4 consecutive value columns of one token)
+    // that each lane ends up with consecutive value columns of one token)
     bf16x8 fk[2][8];
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      // one quarter of the next chunk's copy (and, first, last chunk's o)
-      if (c > c_beg) store_o_tile(a, h, w, nn, grp, o_t0, o_n, s4, o_pend[s4]);
-      if (more) copy_block_part(next_src, next_dst, w, l, s4);
-      if (s4 == 3) {
-        touched = c + 2 < c_end;
-        if (touched) touch_block(chain_blocks + (c + 2) * BLOCK_BYTES, junk[w], tid);
-      }
+      // one token tile of last chunk's o (and, without copy waves, a quarter
+      // of the next chunk's copy)
+      if (c > c_beg) store_o_tile(s4);
+      if (NCP == 0 && c + 1 < c_end)
+        copy_step<C>(chain_blocks + (c + 1) * BLOCK_BYTES, lds[cur ^ 1], w, p, l, s4);
       bf16x8 nw[4], nq[4];
       if (s4 < 3) {
 #pragma unroll
@@ -253,9 +331,9 @@ __global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          vn[mt][q2] = mfma_bf16(fw[mt], hb[s4][q2], vn[mt][q2]);
-          ot[mt][q2] = mfma_bf16(hb[s4][q2], fq[mt], ot[mt][q2]);
+        for (int q = 0; q < TPW; ++q) {
+          vn[mt][q] = mfma_bf16(fw[mt], hb[s4][q], vn[mt][q]);
+          ot[mt][q] = mfma_bf16(hb[s4][q], fq[mt], ot[mt][q]);
         }
       if (s4 < 3) {
 #pragma unroll
@@ -267,13 +345,13 @@ __global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
     }
 
     // v_new as bf16 operands (k slabs of 32 tokens)
-    bf16x8 vb[2][2];
+    bf16x8 vb[2][TPW];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
+      for (int q = 0; q < TPW; ++q)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vb[s2][q2][e] = (bf16_t)vn[2 * s2 + (e >> 2)][q2][e & 3];
+        for (int e = 0; e < 8; ++e) vb[s2][q][e] = (bf16_t)vn[2 * s2 + (e >> 2)][q][e & 3];
 
     // h <- Diag(gamma) h + kg^T v_new   (the serial dependency: first)
     bf16x8 fah[AQK_FRAGS], fal[AQK_FRAGS];
@@ -287,52 +365,69 @@ __global__ __launch_bounds__(REC_THREADS) void recurrence_kernel(RecurArgs a) {
 #pragma unroll
       for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) S[t][q2] = mfma_bf16(fk[s2][t], vb[s2][q2], S[t][q2]);
+        for (int q = 0; q < TPW; ++q) S[t][q] = mfma_bf16(fk[s2][t], vb[s2][q], S[t][q]);
 
     // o^T += v_new^T Aqk^T   (Aqk in hi + lo bf16)
 #pragma unroll
     for (int x = 0; x < AQK_FRAGS; ++x)
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        ot[LT_MT[x]][q2] = mfma_bf16(vb[LT_S[x]][q2], fah[x], ot[LT_MT[x]][q2]);
-        ot[LT_MT[x]][q2] = mfma_bf16(vb[LT_S[x]][q2], fal[x], ot[LT_MT[x]][q2]);
+      for (int q = 0; q < TPW; ++q) {
+        ot[lt_mt(x)][q] = mfma_bf16(vb[lt_s(x)][q], fah[x], ot[lt_mt(x)][q]);
+        ot[lt_mt(x)][q] = mfma_bf16(vb[lt_s(x)][q], fal[x], ot[lt_mt(x)][q]);
       }
 
-    // o^T of this chunk as bf16 (nearest even), stored at the next chunk
+    // o^T of this chunk as bf16 (nearest even), stored during the next one
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
+      for (int q = 0; q < TPW; ++q)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o_pend[mt][4 * q2 + r] = (bf16_t)ot[mt][q2][r];
+        for (int r = 0; r < 4; ++r) o_pend[mt][q][r] = (bf16_t)ot[mt][q][r];
     o_t0 = t0;
     o_n = n;
   }
   if (c_end > c_beg) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) store_o_tile(a, h, w, nn, grp, o_t0, o_n, mt, o_pend[mt]);
+    for (int mt = 0; mt < 4; ++mt) store_o_tile(mt);
   }
-  // no load may still be writing LDS when the workgroup ends
-  __builtin_amdgcn_s_waitcnt(WAIT_ALL);
 
   if (a.hT) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
+      for (int q = 0; q < TPW; ++q)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * t + 4 * grp + r;
-          const int col = VCOL(2 * w + q2, nn);
-          a.hT[st_base + row * DV + col] = S[t][q2][r];
+          const int col = VCOL(nt0 + q, nn);
+          a.hT[st_base + row * DV + col] = S[t][q][r];
         }
   }
+  // no copy may still be writing LDS when the workgroup ends
+  if (NCP == 0) __builtin_amdgcn_s_waitcnt(0);
+}
+
+template <int NC, int NCP, int TPW>
+static hipError_t launch_rec(const RecurArgs &a, int64_t chains, hipStream_t stream) {
+  using C = RecCfg<NC, NCP, TPW>;
+  const int64_t groups = (chains + 7) / 8;  // chains per XCD slot, rounded up
+  const int64_t grid = groups * 8 * C::PARTS;
+  hipLaunchKernelGGL((recurrence_kernel<NC, NCP, TPW>), dim3((unsigned)grid), dim3(C::THREADS), 0,
+                     stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_recurrence(const RecurArgs &a, hipStream_t stream) {
   const int64_t chains = (int64_t)a.N * a.H;
-  hipLaunchKernelGGL(recurrence_kernel, dim3((unsigned)chains), dim3(REC_THREADS), 0, stream, a);
-  return hipGetLastError();
+  if (chains <= 0) return hipSuccess;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  // split each chain over as many workgroups as still fit the device once
+  if (chains * 4 <= cus) return launch_rec<2, 2, 1>(a, chains, stream);
+  if (chains * 2 <= cus) return launch_rec<4, 2, 1>(a, chains, stream);
+  return launch_rec<4, 0, 2>(a, chains, stream);
 }
 
 }  // namespace kda
