@@ -51,8 +51,9 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 //          halves (hi fragments first).  Only the six (mt, s) fragments with
 //          any j <= i are stored, indexed by AQK_IDX.
 //   U    : U as the C-tile initialiser of v_new: [value tile nt 0..7][token
-//          tile mt 0..3] tiles of 64 lanes x 4 bf16 (C layout); lane (n, grp)
-//          element r holds U[16 mt + 4 grp + r][VCOL(nt, n)].  VCOL permutes
+//          tile pair 0..1] entries of 64 lanes x 16 bytes; bytes 8 m .. 8 m + 7
+//          of lane (n, grp) hold the C tile of token tile mt = 2 pair + m,
+//          element r = U[16 mt + 4 grp + r][VCOL(nt, n)] (bf16).  VCOL permutes
 //          the value columns inside each 32-column slice so that the
 //          recurrence's transposed output tiles give every lane 8
 //          consecutive columns of a token (one 16-byte store).
@@ -65,7 +66,11 @@ constexpr int OFF_KGT = OFF_QG + 16 * FRAG_BYTES;
 constexpr int OFF_AQK = OFF_KGT + 16 * FRAG_BYTES;
 constexpr int AQK_FRAGS = 6;
 constexpr int OFF_U = OFF_AQK + 2 * AQK_FRAGS * FRAG_BYTES;
-constexpr int UTILE_BYTES = 64 * 8;
+constexpr int UTILE_BYTES = 64 * 8;  // one value tile x token tile C tile (bf16)
+// byte offset of U's C tile (value tile nt, token tile mt) for lane l
+__host__ __device__ constexpr int U_OFFSET(int nt, int mt, int l) {
+  return OFF_U + ((nt * 2 + (mt >> 1)) * 64 + l) * 16 + (mt & 1) * 8;
+}
 constexpr int OFF_GAM = OFF_U + 32 * UTILE_BYTES;
 constexpr int BLOCK_BYTES = OFF_GAM + DK * 4;
 static_assert(BLOCK_BYTES % 256 == 0, "intermediate blocks stay 256-byte aligned");

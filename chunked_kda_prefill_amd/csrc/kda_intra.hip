@@ -158,22 +158,29 @@ struct UnitInputs {
 // lane loads, back to back, without branches) and zeroed where they are
 // used, through row_mask().
 __device__ __forceinline__ void load_unit(const IntraArgs &a, const int4 info, int h, int row,
-                                          int grp, UnitInputs &in) {
+                                          int grp, UnitInputs &in, int part = -1) {
   // the chunk table is written by the same call; clamping keeps even a
   // corrupted one in bounds
-  in.t0 = info.x < 0 ? 0 : (info.x > a.T ? a.T : info.x);
-  in.n = (int)(info.y < 0 ? 0 : (info.y > a.T - in.t0 ? a.T - in.t0 : (info.y > BT ? BT : info.y)));
-  const bool ok = row < in.n;
-  const int64_t t = ok ? in.t0 + row : (in.t0 < a.T ? in.t0 : a.T - 1);
+  const int64_t t0 = info.x < 0 ? 0 : (info.x > a.T ? a.T : info.x);
+  const int n = (int)(info.y < 0 ? 0 : (info.y > a.T - t0 ? a.T - t0 : (info.y > BT ? BT : info.y)));
+  const bool ok = row < n;
+  const int64_t t = ok ? t0 + row : (t0 < a.T ? t0 : a.T - 1);
   const int64_t off = (t * a.H + h) * DK;
+  if (part <= 0) {
+    in.t0 = t0;
+    in.n = n;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int ch = slot_ch(j, grp);
-    in.q[j] = *reinterpret_cast<const uint2 *>(a.q + off + ch);
-    in.k[j] = *reinterpret_cast<const uint2 *>(a.k + off + ch);
-    in.g[j] = *reinterpret_cast<const float4 *>(a.g + off + ch);
+    for (int j = 0; j < 8; ++j) in.g[j] = *reinterpret_cast<const float4 *>(a.g + off + slot_ch(j, grp));
+    in.beta = a.beta[t * a.H + h];
   }
-  in.beta = a.beta[t * a.H + h];
+  if (part < 0 || part == 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) in.q[j] = *reinterpret_cast<const uint2 *>(a.q + off + slot_ch(j, grp));
+  }
+  if (part < 0 || part == 2) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) in.k[j] = *reinterpret_cast<const uint2 *>(a.k + off + slot_ch(j, grp));
+  }
 }
 
 __device__ __forceinline__ uint32_t row_mask(int row, int n) { return row < n ? 0xffffffffu : 0u; }
@@ -326,7 +333,11 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
 
   // Epilogue of strip block (ba, bb): Aqk^T half to the block, L (times
   // beta_i) to LDS; returns the L values the lane holds.
-  auto strip_out = [&](int ba, int bb, const f32x4 &accA, const f32x4 &accL, f32x4 &lv) {
+  // With zero_upper (a diagonal block in half 0 of its fragment) the
+  // fragment's other half, above the diagonal, is written as zeros in the
+  // same 16-byte store.
+  auto strip_out = [&](int ba, int bb, const f32x4 &accA, const f32x4 &accL, f32x4 &lv,
+                       bool zero_upper) {
     bf16x4 ah, al;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -334,8 +345,15 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
       split_bf16(keep ? accA[r] * a.scale : 0.f, ah, al, r);
     }
     const int idx = AQK_IDX(ba, bb >> 1), half = bb & 1;
-    store_bf16x4(blk + OFF_AQK + (idx * 64 + l) * 16 + half * 8, ah);
-    store_bf16x4(blk + OFF_AQK + ((AQK_FRAGS + idx) * 64 + l) * 16 + half * 8, al);
+    if (zero_upper) {
+      const bf16_t z = (bf16_t)0.f;
+      store_bf16x8(blk + OFF_AQK + (idx * 64 + l) * 16, bf16x8{ah[0], ah[1], ah[2], ah[3], z, z, z, z});
+      store_bf16x8(blk + OFF_AQK + ((AQK_FRAGS + idx) * 64 + l) * 16,
+                   bf16x8{al[0], al[1], al[2], al[3], z, z, z, z});
+    } else {
+      store_bf16x4(blk + OFF_AQK + (idx * 64 + l) * 16 + half * 8, ah);
+      store_bf16x4(blk + OFF_AQK + ((AQK_FRAGS + idx) * 64 + l) * 16 + half * 8, al);
+    }
     const f32x4 bv = as_f32x4(*reinterpret_cast<const float4 *>(&sm.beta[SB * ba + 4 * grp]));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -357,18 +375,13 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
     }
   }
   f32x4 Ld;  // L_ww (masked, beta-scaled) for the inverse
-  strip_out(w, w, accA, accL, Ld);
-  if ((w & 1) == 0) {
-    // the other half of the diagonal slab lies above the diagonal
-    const bf16x4 z = {(bf16_t)0.f, (bf16_t)0.f, (bf16_t)0.f, (bf16_t)0.f};
-    const int idx = AQK_IDX(w, w >> 1);
-    store_bf16x4(blk + OFF_AQK + (idx * 64 + l) * 16 + 8, z);
-    store_bf16x4(blk + OFF_AQK + ((AQK_FRAGS + idx) * 64 + l) * 16 + 8, z);
-  }
+  // (the other half of an even diagonal block's slab lies above the diagonal)
+  strip_out(w, w, accA, accL, Ld, (w & 1) == 0);
   __syncthreads();
 
-  // ---- the unit's q, k, g are consumed: start the next unit's loads ----
-  if (un < units) load_unit(a, info_next, (int)(un % a.H), row, grp, nxt);
+  // ---- the unit's q, k, g are consumed: start the next unit's loads (in
+  // three parts, spread over the phases so no phase issues a burst) ----
+  if (un < units) load_unit(a, info_next, (int)(un % a.H), row, grp, nxt, 0);
 
   // ---- off-diagonal strip blocks, two at most per wave:
   //   wave 0: (3,0)   wave 1: (1,0) (3,1)   wave 2: (2,0) (2,1)   wave 3: (3,2)
@@ -424,10 +437,12 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
       }
     }
     f32x4 unused;
-    strip_out(ba0, bb0, accA0, accL0, unused);
-    if (two) strip_out(ba1, bb1, accA1, accL1, unused);
+    strip_out(ba0, bb0, accA0, accL0, unused, false);
+    if (two) strip_out(ba1, bb1, accA1, accL1, unused, false);
   }
   __syncthreads();
+
+  if (un < units) load_unit(a, info_next, (int)(un % a.H), row, grp, nxt, 1);
 
   // ---- this unit's V (only U needs it, at the end) ----
   uint2 vrow[8];
@@ -478,6 +493,8 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
     for (int r = 0; r < 4; ++r) sm.tt[sw_lt(d0 + 4 * grp + r, d0 + nn)] = PC[r];
   }
   __syncthreads();
+
+  if (un < units) load_unit(a, info_next, (int)(un % a.H), row, grp, nxt, 2);
 
   // ---- column w of T below the diagonal, top-down:
   // T_ab = -T_aa sum_{c=b}^{a-1} L_ac T_cb  with b = w, a = w + o ----
@@ -582,51 +599,60 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
       }
     }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4 acc = zero4();
+    for (int mp = 0; mp < 2; ++mp) {
+      bf16x8 uv;
 #pragma unroll
-      for (int s = 0; s <= (mt >> 1); ++s) {
-        const int x = AQK_IDX(mt, s);
-        acc = mfma_bf16(th(x), vb[s], acc);
-        acc = mfma_bf16(tl(x), vb[s], acc);
+      for (int m = 0; m < 2; ++m) {
+        const int mt = 2 * mp + m;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s <= (mt >> 1); ++s) {
+          const int x = AQK_IDX(mt, s);
+          acc = mfma_bf16(th(x), vb[s], acc);
+          acc = mfma_bf16(tl(x), vb[s], acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) uv[4 * m + r] = (bf16_t)acc[r];
       }
-      bf16x4 uv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) uv[r] = (bf16_t)acc[r];
-      store_bf16x4(blk + OFF_U + ((nt * 4 + mt) * 64 + l) * 8, uv);
-    }
-  }
+      store_bf16x8(blk + U_OFFSET(nt, 2 * mp, l), uv);
+    }  }
 
-  // ---- W^T = (K*Gamma)^T T'^T: wave w owns key tiles 2w and 2w+1 ----
+  // ---- W^T = (K*Gamma)^T T'^T: wave w owns key tiles 2w and 2w+1, which
+  // are the two halves of key slab w's fragments: one 16-byte store each ----
+  {
+    bf16x8 kb[2][2];
 #pragma unroll
-  for (int q2 = 0; q2 < 2; ++q2) {
-    const int mtc = 2 * w + q2;
-    bf16x8 kb[2];
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int mtc = 2 * w + q2;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bf16x4 lo4 = tr4(kgmt, 32 * s + 8 * grp, 16 * mtc);
-      const bf16x4 hi4 = tr4(kgmt, 32 * s + 8 * grp + 4, 16 * mtc);
+      for (int s = 0; s < 2; ++s) {
+        const bf16x4 lo4 = tr4(kgmt, 32 * s + 8 * grp, 16 * mtc);
+        const bf16x4 hi4 = tr4(kgmt, 32 * s + 8 * grp + 4, 16 * mtc);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kb[s][e] = lo4[e];
-        kb[s][4 + e] = hi4[e];
+        for (int e = 0; e < 4; ++e) {
+          kb[q2][s][e] = lo4[e];
+          kb[q2][s][4 + e] = hi4[e];
+        }
       }
     }
 #pragma unroll
     for (int nti = 0; nti < 4; ++nti) {
-      f32x4 acc = zero4();
+      bf16x8 wv;
 #pragma unroll
-      for (int s = 0; s <= (nti >> 1); ++s) {
-        const int x = AQK_IDX(nti, s);
-        acc = mfma_bf16(kb[s], th(x), acc);
-        acc = mfma_bf16(kb[s], tl(x), acc);
+      for (int q2 = 0; q2 < 2; ++q2) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int s = 0; s <= (nti >> 1); ++s) {
+          const int x = AQK_IDX(nti, s);
+          acc = mfma_bf16(kb[q2][s], th(x), acc);
+          acc = mfma_bf16(kb[q2][s], tl(x), acc);
+        }
+        // lane holds W^T[16 (2w + q2) + 4grp + r][16 nti + nn] -> -W, half q2
+        // of the fragment (token tile nti, key slab w)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wv[4 * q2 + r] = (bf16_t)(-acc[r]);
       }
-      // lane holds W^T[16 mtc + 4grp + r][16 nti + nn] -> -W, half (mtc & 1)
-      // of the fragment (token tile nti, key slab mtc >> 1)
-      bf16x4 wv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) wv[r] = (bf16_t)(-acc[r]);
-      store_bf16x4(blk + OFF_WN + ((nti * 4 + (mtc >> 1)) * 64 + l) * 16 + (mtc & 1) * 8, wv);
+      store_bf16x8(blk + OFF_WN + ((nti * 4 + w) * 64 + l) * 16, wv);
     }
   }
 }

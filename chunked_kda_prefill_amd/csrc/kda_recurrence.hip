@@ -283,8 +283,7 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int q = 0; q < TPW; ++q) {
-        const bf16x4 u = *reinterpret_cast<const bf16x4 *>(
-            blk + OFF_U + (((nt0 + q) * 4 + mt) * 64 + l) * 8);
+        const bf16x4 u = *reinterpret_cast<const bf16x4 *>(blk + U_OFFSET(nt0 + q, mt, l));
 #pragma unroll
         for (int r = 0; r < 4; ++r) vn[mt][q][r] = (float)u[r];
         ot[mt][q] = zero4();

@@ -63,12 +63,13 @@ def decode_block(raw: np.ndarray) -> dict:
             for e in range(8):
                 AQK[16 * mt + n, _perm_index(s, grp, e)] = hi[l, e] + lo[l, e]
     for nt in range(8):
-        for mt in range(4):
-            off = OFF_U + ((nt * 4 + mt) * 64) * 8
-            t = _bf16(raw[off:off + 512]).reshape(64, 4)
+        for mp in range(2):
+            off = OFF_U + ((nt * 2 + mp) * 64) * 16
+            t = _bf16(raw[off:off + 1024]).reshape(64, 8)
             for l in range(64):
                 n, grp = l & 15, l >> 4
-                for r in range(4):
-                    U[16 * mt + 4 * grp + r, _vcol(nt, n)] = t[l, r]
+                for m in range(2):
+                    for r in range(4):
+                        U[16 * (2 * mp + m) + 4 * grp + r, _vcol(nt, n)] = t[l, 4 * m + r]
     gam = raw[OFF_GAM:OFF_GAM + 512].view(np.float32).astype(np.float64)
     return {"W": W, "qg": QG, "kg": KG, "Aqk": AQK, "U": U, "gamma": gam}
