@@ -177,7 +177,7 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(w.name, dom),
-                "kernel_us": {"kda_intra(+chunk_table)": round(intra_us, 2),
+                "kernel_us": {"kda_intra": round(intra_us, 2),
                               "kda_recurrence": round(rec_us, 2)},
                 "kernel_bytes_per_launch": {"kda_intra": intra_bytes,
                                             "kda_recurrence": rec_bytes}}

@@ -2,6 +2,7 @@
 // the caller's stream.  Nothing here reads device memory, allocates, or
 // synchronises.
 #include "kda.h"
+#include "kda_chunk_table.h"
 #include "kda_internal.h"
 #include "kda_launch.h"
 
@@ -164,23 +165,31 @@ static kda_status run_recurrence(const float *initial_state, int64_t T, int32_t 
 static kda_status run_intra(const void *q, const void *k, const void *v, const float *g,
                             const float *beta, const int32_t *cu_seqlens, int64_t T, int32_t N,
                             int32_t H, float scale, const Ws &ws, hipStream_t stream) {
-  hipError_t e = launch_chunk_table(cu_seqlens, T, N, ws.L.nc_max, ws.chunk_first, ws.chunk_info,
-                                    ws.flags, stream);
-  if (e != hipSuccess) return KDA_ERR_HIP;
+  // small batches: the intra-chunk kernel builds the chunk table itself (one
+  // launch less); larger ones get the standalone table kernel first
+  const bool inline_table = N <= INLINE_SEQS && ws.L.nc_max > 0;
+  if (!inline_table) {
+    hipError_t e = launch_chunk_table(cu_seqlens, T, N, ws.L.nc_max, ws.chunk_first,
+                                      ws.chunk_info, ws.flags, stream);
+    if (e != hipSuccess) return KDA_ERR_HIP;
+  }
   IntraArgs ia;
   ia.q = static_cast<const uint16_t *>(q);
   ia.k = static_cast<const uint16_t *>(k);
   ia.v = static_cast<const uint16_t *>(v);
   ia.g = g;
   ia.beta = beta;
+  ia.cu = cu_seqlens;
   ia.chunk_first = ws.chunk_first;
   ia.chunk_info = ws.chunk_info;
+  ia.flags = ws.flags;
   ia.blocks = ws.blocks;
   ia.nc_max = ws.L.nc_max;
   ia.T = T;
   ia.N = N;
   ia.H = H;
   ia.scale = scale;
+  ia.inline_table = inline_table ? 1 : 0;
   return hip_status(launch_intra(ia, stream));
 }
 

@@ -42,6 +42,7 @@
 // lower (X^16 = 0); then wave b fills column b of T top-down,
 // T_ab = -T_aa sum_{c=b}^{a-1} L_ac T_cb, needing only the other waves'
 // diagonal blocks.  All of it runs in fp32 on v_mfma_f32_16x16x4_f32.
+#include "kda_chunk_table.h"
 #include "kda_cumsum.h"
 #include "kda_internal.h"
 #include "kda_launch.h"
@@ -93,6 +94,18 @@ __device__ __forceinline__ int32_t chunk_count(const int32_t *chunk_first, int N
   return ((const __attribute__((address_space(4))) int32_t *)(uintptr_t)chunk_first)[N];
 }
 
+// Record of chunk c: from the workspace table, or (inline_table) computed
+// from the chunk offsets in LDS.  `s` is a running sequence index: the
+// chunks a workgroup visits only increase, so it only moves forward.
+__device__ __forceinline__ int4 unit_record(const IntraArgs &a, const int32_t *first_lds, int64_t c,
+                                            int &s) {
+  if (!a.inline_table) return chunk_record(a.chunk_info, c);
+  while (s + 1 < a.N && first_lds[s + 1] <= c) ++s;
+  return chunk_record_of(
+      (const int32_t *)((const __attribute__((address_space(4))) int32_t *)(uintptr_t)a.cu), a.T,
+      first_lds, s, c);
+}
+
 struct __align__(16) IntraSmem {
   // k~ (fp32 [64][128]) for the strips; then the kg and K*Gamma bf16 tiles
   // (first and second half); then V (bf16) where kg was
@@ -102,7 +115,8 @@ struct __align__(16) IntraSmem {
   float tab[TAB_ROWS][DK];
   float beta[BT];
 };
-static_assert(sizeof(IntraSmem) <= 80 * 1024, "two units fit one CU's LDS");
+static_assert(sizeof(IntraSmem) + 4 * (INLINE_SEQS + 1) <= 80 * 1024, "two units fit one CU's LDS");
+static_assert(sizeof(TableScratch) <= sizeof(float) * BT * DK, "table scratch fits where k~ goes");
 
 __device__ __forceinline__ void store_bf16x4(uint8_t *p, const bf16x4 &x) {
   *reinterpret_cast<bf16x4 *>(p) = x;
@@ -208,7 +222,8 @@ __device__ __forceinline__ void load_v(const IntraArgs &a, int64_t t0, int n, in
 // One (chunk, head) unit whose inputs are already in `nxt` (loads issued).
 // After the unit's own inputs are consumed, `nxt` receives the next unit's.
 __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, int64_t u,
-                                           int64_t units, UnitInputs &nxt) {
+                                           int64_t units, UnitInputs &nxt, const int32_t *first_lds,
+                                           int &s_next) {
   // threadIdx.x through an opaque move, so that address arithmetic derived
   // from it stays inside the unit loop instead of being hoisted out of it
   int tid;
@@ -220,7 +235,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   // the next unit's chunk record, fetched now so that its data loads can be
   // issued later without waiting on it
   const int64_t un = u + gridDim.x;
-  const int4 info_next = chunk_record(a.chunk_info, (un < units ? un : u) / a.H);
+  const int4 info_next = unit_record(a, first_lds, (un < units ? un : u) / a.H, s_next);
   UnitInputs in = nxt;
   const int n = in.n;
   uint8_t *blk = a.blocks + ((int64_t)h * a.nc_max + c) * BLOCK_BYTES;
@@ -664,17 +679,38 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void intra_kernel(
     IntraArgs a) {
   __shared__ IntraSmem sm;
-  if (a.T <= 0) return;
-  int64_t nc = chunk_count(a.chunk_first, a.N);
+  __shared__ int32_t first_lds[INLINE_SEQS + 1];
+  int64_t nc;
+  if (a.inline_table) {
+    // every workgroup builds the chunk offsets (its scratch lives where k~
+    // will be); workgroup 0 also writes the workspace table
+    chunk_table_build(a.cu, a.T, a.N, a.nc_max, blockIdx.x == 0, a.chunk_first, a.chunk_info,
+                      a.flags, first_lds, *reinterpret_cast<TableScratch *>(sm.x));
+    nc = first_lds[a.N];
+  } else {
+    nc = chunk_count(a.chunk_first, a.N);
+  }
   nc = nc < 0 ? 0 : (nc > a.nc_max ? a.nc_max : nc);
   const int64_t units = nc * a.H;
   int64_t u = blockIdx.x;
   if (u >= units) return;
   const int tid = threadIdx.x;
+  // running sequence index: the last sequence whose first chunk is at or
+  // before this workgroup's first chunk (binary search once)
+  int s_next = 0;
+  if (a.inline_table) {
+    const int64_t c0 = u / a.H;
+    int lo = 0, hi = a.N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (first_lds[mid] <= c0) lo = mid; else hi = mid - 1;
+    }
+    s_next = lo;
+  }
   UnitInputs nxt;
-  load_unit(a, chunk_record(a.chunk_info, u / a.H), (int)(u % a.H), SB * (tid >> 6) + (tid & 15),
-            (tid >> 4) & 3, nxt);
-  for (; u < units; u += gridDim.x) intra_unit(a, sm, u, units, nxt);
+  load_unit(a, unit_record(a, first_lds, u / a.H, s_next), (int)(u % a.H),
+            SB * (tid >> 6) + (tid & 15), (tid >> 4) & 3, nxt);
+  for (; u < units; u += gridDim.x) intra_unit(a, sm, u, units, nxt, first_lds, s_next);
 }
 
 hipError_t launch_intra(const IntraArgs &a, hipStream_t stream) {

@@ -84,6 +84,17 @@ def test_long_single_sequence(dev):
     parity(o[:, heads], f[:, heads], o_ref, f_ref, "long")
 
 
+@pytest.mark.parametrize("N", [1024, 1100], ids=["N1024_table_in_intra", "N1100_table_kernel"])
+def test_many_sequences(dev, N):
+    # up to 1024 sequences the intra-chunk kernel builds the chunk table
+    # itself; past that a separate table kernel does: both sides of the switch
+    lens = list(np.random.default_rng(5).integers(0, 140, size=N))
+    w = wl.make_workload(f"many_N{N}", lens, H=2, seed=44, h0="normal")
+    log(f"[case] many sequences N={N} T={w.T} chunks={w.num_chunks()}")
+    o, f = run_gpu(w, dev)
+    parity(o, f, *run_oracle(w), f"many N={N}")
+
+
 # ---------------------------------------------------------------------------
 # varlen bit-exactness
 # ---------------------------------------------------------------------------

@@ -71,6 +71,61 @@ def test_chunk_table_clamps_malformed_offsets(dev):
     assert np.all(info[:nc, 0] >= 0) and np.all(info[:nc, 0] + info[:nc, 1] <= T)
 
 
+@pytest.mark.parametrize("lens", CU_CASES + [list(np.random.default_rng(6).integers(0, 90, size=n))
+                                             for n in (1024, 1025)],
+                         ids=lambda x: f"N{len(x)}")
+def test_chunk_table_in_workspace(dev, lens):
+    # the table the forward pass leaves in its workspace (built inside the
+    # intra-chunk kernel for up to 1024 sequences, by its own kernel above)
+    import torch
+    import chunked_kda_prefill_amd as kda
+    w = wl.make_workload(f"table_N{len(lens)}", lens, H=1, seed=34)
+    log(f"[workspace table] N={w.N} T={w.T}")
+    t = wl.to_torch(w, dev)
+    ws = kda.new_workspace(w.T, w.N, w.H, dev).fill_(0xA5)    # no stale table to pass on
+    kda.chunk_intra(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
+                    scale=w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    lay = kda.workspace_layout(w.T, w.N, w.H)
+    raw = ws.cpu().numpy()
+    flags = raw[lay["flags"]:lay["flags"] + 4].view(np.int32)
+    first = raw[lay["chunk_first"]:lay["chunk_first"] + 4 * (w.N + 1)].view(np.int32)
+    info = raw[lay["chunk_info"]:lay["chunk_info"] + 16 * lay["nc_max"]].view(np.int32)
+    info = info.reshape(-1, 4)
+    rows = oracle.chunk_table(w.cu_seqlens)
+    nc = len(rows)
+    assert int(flags[0]) == 0
+    counts = [(int(L) + 63) // 64 for L in lens]
+    assert list(first) == list(np.concatenate([[0], np.cumsum(counts)]))
+    exp = np.array([[r["start"], r["length"], r["seq"], r["local"]] for r in rows],
+                   dtype=np.int32).reshape(-1, 4)
+    assert np.array_equal(info[:nc], exp)
+    assert np.all(info[nc:] == np.array([0, 0, -1, -1]))
+
+
+def test_chunk_table_in_workspace_clamps_malformed_offsets(dev):
+    # the same clamping when the intra-chunk kernel builds the table
+    import torch
+    import chunked_kda_prefill_amd as kda
+    w = wl.make_workload("table_malformed", [100, 100], H=1, seed=35)
+    t = wl.to_torch(w, dev)
+    cu = torch.tensor([0, 100, 40, 300], dtype=torch.int32, device=dev)
+    T, N = 200, 3
+    log("[workspace table] malformed cu")
+    ws = kda.new_workspace(T, N, 1, dev).fill_(0xA5)
+    kda.chunk_intra(t["q"], t["k"], t["v"], t["g"], t["beta"], cu, scale=w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    lay = kda.workspace_layout(T, N, 1)
+    raw = ws.cpu().numpy()
+    assert int(raw[lay["flags"]:lay["flags"] + 4].view(np.int32)[0]) == 1
+    first = raw[lay["chunk_first"]:lay["chunk_first"] + 4 * (N + 1)].view(np.int32)
+    info = raw[lay["chunk_info"]:lay["chunk_info"] + 16 * lay["nc_max"]].view(np.int32)
+    info = info.reshape(-1, 4)
+    nc = int(first[-1])
+    assert nc <= lay["nc_max"]
+    assert np.all(info[:nc, 0] >= 0) and np.all(info[:nc, 0] + info[:nc, 1] <= T)
+
+
 @pytest.mark.parametrize("lens", [[256], [70, 130, 1, 64], [3, 200]], ids=str)
 def test_gate_cumsum(dev, lens):
     import torch
