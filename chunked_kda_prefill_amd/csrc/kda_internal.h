@@ -35,6 +35,15 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Word 3 of a raw buffer resource on gfx950 (32-bit data format, no
+// swizzle).  With stride 0 the hardware range check compares each lane's
+// byte offset with the record count, and out-of-range lanes read zero and
+// write nothing.
+constexpr int BUF_DWORD3 = 0x00020000;
+// Cache-policy operand of buffer loads and stores: non-temporal.
+constexpr int CPOL_NT = 2;
 
 // ---------------------------------------------------------------------------
 // Per-(head, chunk) intermediate block written by the intra-chunk kernel and

@@ -158,13 +158,46 @@ __device__ __forceinline__ f32x4 mm16(const f32x4 &At, const f32x4 &B, f32x4 acc
 
 }  // namespace
 
+// Input loads go through raw buffer resources based at the unit's first row
+// (wave-uniform, so they live in scalar registers and every lane's address
+// is a 32-bit offset).  v is read non-temporally: measured on the headline
+// batch, that alone keeps the last-level cache from dropping the
+// intermediate blocks the recurrence reads next (its time fell from ~70 to
+// ~53 us), while non-temporal q and g reads slowed this kernel down.
+constexpr int AUX_G = 0, AUX_QK = 0, AUX_V = CPOL_NT;
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// Buffer over rows [tb, tb + 64) of a [T, H, 128] tensor (clamped to T).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_rsrc(const void *base, int64_t tb, int64_t T,
+                                                             int H, int h, int elem) {
+  const int64_t rows = T - tb < BT ? T - tb : BT;
+  const char *p = static_cast<const char *>(base) + ((tb * H + h) * DK) * elem;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), 0, (int)(rows * H * DK * elem),
+                                           BUF_DWORD3);
+}
+
+// bf16 rows are read 16 bytes per lane: for key slab s (32 channels) lane
+// group grp reads the 4-channel groups 2m and 2m+1, m = load_m(grp), and a
+// permlane16 swap between lane groups (0,1) and (2,3) turns them into the
+// groups grp and grp + 4 that the channel slots hold (slot_ch(2s, grp) and
+// slot_ch(2s + 1, grp)).
+__device__ __forceinline__ int load_m(int grp) { return ((grp & 1) << 1) | (grp >> 1); }
+__device__ __forceinline__ void slab_to_slots(const u32x4 &raw, uint2 &lo, uint2 &hi) {
+  const u32x2 a = __builtin_bit_cast(u32x2, __builtin_amdgcn_permlane16_swap(raw.x, raw.z, false, false));
+  const u32x2 b = __builtin_bit_cast(u32x2, __builtin_amdgcn_permlane16_swap(raw.y, raw.w, false, false));
+  lo = make_uint2(a.x, b.x);
+  hi = make_uint2(a.y, b.y);
+}
+
 // Inputs of one (chunk, head) unit for one lane: row `row`, the channel
-// slots of kda_cumsum.h.  Loaded into registers ahead of use.
+// slots of kda_cumsum.h (q and k as loaded: slab_to_slots() gives the
+// slots).  Loaded into registers ahead of use.
 struct UnitInputs {
   int64_t t0;
   int n;
-  uint2 q[8], k[8];  // 4 bf16 each, channels slot_ch(j, grp) + 0..3
-  float4 g[8];
+  u32x4 q[4], k[4];  // per key slab: channels 32 s + 8 load_m(grp) + 0..7
+  float4 g[8];       // channels slot_ch(j, grp) + 0..3
   float beta;
 };
 
@@ -177,23 +210,34 @@ __device__ __forceinline__ void load_unit(const IntraArgs &a, const int4 info, i
   // corrupted one in bounds
   const int64_t t0 = info.x < 0 ? 0 : (info.x > a.T ? a.T : info.x);
   const int n = (int)(info.y < 0 ? 0 : (info.y > a.T - t0 ? a.T - t0 : (info.y > BT ? BT : info.y)));
-  const bool ok = row < n;
-  const int64_t t = ok ? t0 + row : (t0 < a.T ? t0 : a.T - 1);
-  const int64_t off = (t * a.H + h) * DK;
+  const int64_t tb = t0 < a.T ? t0 : a.T - 1;  // first row of the unit's buffers
+  const int r = row < n ? row : 0;               // row within them
+  const int roff = r * a.H * DK;                 // < 2^23 elements: H <= 65535
   if (part <= 0) {
     in.t0 = t0;
     in.n = n;
+    const __amdgpu_buffer_rsrc_t rg = unit_rsrc(a.g, tb, a.T, a.H, h, 4);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) in.g[j] = *reinterpret_cast<const float4 *>(a.g + off + slot_ch(j, grp));
-    in.beta = a.beta[t * a.H + h];
+    for (int j = 0; j < 8; ++j)
+      in.g[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rg, 4 * (roff + slot_ch(j, grp)), 0, AUX_G));
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a.beta + tb * a.H + h), 0, (int)((a.T - tb) * a.H * 4), BUF_DWORD3);
+    in.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * r * a.H, 0, AUX_G));
   }
   if (part < 0 || part == 1) {
+    const __amdgpu_buffer_rsrc_t rq = unit_rsrc(a.q, tb, a.T, a.H, h, 2);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) in.q[j] = *reinterpret_cast<const uint2 *>(a.q + off + slot_ch(j, grp));
+    for (int s = 0; s < 4; ++s)
+      in.q[s] = __builtin_amdgcn_raw_buffer_load_b128(rq, 2 * (roff + 32 * s + 8 * load_m(grp)), 0,
+                                                      AUX_QK);
   }
   if (part < 0 || part == 2) {
+    const __amdgpu_buffer_rsrc_t rk = unit_rsrc(a.k, tb, a.T, a.H, h, 2);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) in.k[j] = *reinterpret_cast<const uint2 *>(a.k + off + slot_ch(j, grp));
+    for (int s = 0; s < 4; ++s)
+      in.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rk, 2 * (roff + 32 * s + 8 * load_m(grp)), 0,
+                                                      AUX_QK);
   }
 }
 
@@ -204,19 +248,17 @@ __device__ __forceinline__ float4 masked(float4 x, uint32_t m) {
                      __uint_as_float(__float_as_uint(x.z) & m), __uint_as_float(__float_as_uint(x.w) & m));
 }
 
-// V rows of the lane (needed only for U, so loaded late); rows past n are
-// zero.
+// V rows of the lane (needed only for U, so loaded late), 16 bytes per
+// key slab: channels 32 s + 8 load_m(grp) + 0..7.  Rows past n are zeroed
+// where they are used.
 __device__ __forceinline__ void load_v(const IntraArgs &a, int64_t t0, int n, int h, int row,
-                                       int grp, uint2 (&v)[8]) {
-  const bool ok = row < n;
-  const int64_t t = ok ? t0 + row : (t0 < a.T ? t0 : a.T - 1);
-  const int64_t off = (t * a.H + h) * DK;
-  const uint32_t m = ok ? 0xffffffffu : 0u;
+                                       int grp, u32x4 (&v)[4]) {
+  const int64_t tb = t0 < a.T ? t0 : a.T - 1;
+  const int roff = (row < n ? row : 0) * a.H * DK;
+  const __amdgpu_buffer_rsrc_t rv = unit_rsrc(a.v, tb, a.T, a.H, h, 2);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint2 vv = *reinterpret_cast<const uint2 *>(a.v + off + slot_ch(j, grp));
-    v[j] = make_uint2(vv.x & m, vv.y & m);
-  }
+  for (int s = 0; s < 4; ++s)
+    v[s] = __builtin_amdgcn_raw_buffer_load_b128(rv, 2 * (roff + 32 * s + 8 * load_m(grp)), 0, AUX_V);
 }
 
 // One (chunk, head) unit whose inputs are already in `nxt` (loads issued).
@@ -238,6 +280,12 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   const int4 info_next = unit_record(a, first_lds, (un < units ? un : u) / a.H, s_next);
   UnitInputs in = nxt;
   const int n = in.n;
+  uint2 qs[8], ks[8];  // q and k in the channel slots
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    slab_to_slots(in.q[s], qs[2 * s], qs[2 * s + 1]);
+    slab_to_slots(in.k[s], ks[2 * s], ks[2 * s + 1]);
+  }
   uint8_t *blk = a.blocks + ((int64_t)h * a.nc_max + c) * BLOCK_BYTES;
   float *rt = sm.tt;  // [0, 4 DK): reference rows; [4 DK, 8 DK): subblock totals
   const uint32_t rmask = row_mask(row, n);
@@ -308,8 +356,8 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
       const float qv[4] = {Q.x, Q.y, Q.z, Q.w};
       const float d[4] = {G[j].x - r7.x, G[j].y - r7.y, G[j].z - r7.z, G[j].w - r7.w};
       float qf[4], kf[4], kgv[4], kmv[4], ktv[4];
-      unpack4(masked(in.q[j], rmask), qf);
-      unpack4(masked(in.k[j], rmask), kf);
+      unpack4(masked(qs[j], rmask), qf);
+      unpack4(masked(ks[j], rmask), kf);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float t = d[e] * LOG2E;
@@ -460,7 +508,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   if (un < units) load_unit(a, info_next, (int)(un % a.H), row, grp, nxt, 1);
 
   // ---- this unit's V (only U needs it, at the end) ----
-  uint2 vrow[8];
+  u32x4 vrow[4];
   load_v(a, in.t0, in.n, h, row, grp, vrow);
 
   // ---- kg and K*Gamma rows into bf16 tiles where k~ was ----
@@ -588,8 +636,8 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   }
   bf16_t *vt = kgt;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    *reinterpret_cast<uint2 *>(&vt[sw_bf16(row, slot_ch(j, grp))]) = vrow[j];
+  for (int s = 0; s < 4; ++s)
+    *reinterpret_cast<u32x4 *>(&vt[sw_bf16(row, 32 * s + 8 * load_m(grp))]) = vrow[s] & rmask;
   __syncthreads();
 
   auto th = [&](int x) { return *reinterpret_cast<const bf16x8 *>(&tfr[(x * 64 + l) * 8]); };

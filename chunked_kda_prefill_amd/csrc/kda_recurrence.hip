@@ -58,13 +58,9 @@ __device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *lds_wave_base
                : "memory", "m0");
 }
 
-__device__ __forceinline__ void dma4(const uint8_t *src, uint8_t *lds_wave_base) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :
-               : "v"(src), "s"(base)
-               : "memory", "m0");
-}
+// s_waitcnt immediate that waits for LDS (and scalar) accesses only:
+// vmcnt and expcnt at their maxima, lgkmcnt 0
+constexpr int LGKM_ONLY = 0xF | (0x7 << 4) | (0x3 << 14);
 
 constexpr int ROUND = 1024;                  // one wave's copy: 64 lanes x 16 bytes
 constexpr int SHARED_ROUNDS = OFF_U / ROUND;  // -W, qg, kg^T, Aqk: every part needs them
@@ -82,6 +78,12 @@ struct RecCfg {
   // shared fragments, this part's U tiles, and gamma (half a round)
   static constexpr int ROUNDS = SHARED_ROUNDS + U_ROUNDS + 1;
   static_assert(TILES * PARTS == 8, "parts cover the 128 value columns");
+  // o of a chunk (64 tokens x 16 TILES columns, bf16) is staged in LDS for
+  // the copy waves to store, in another part's U tiles of the block buffer
+  // (never copied by this workgroup)
+  static constexpr int O_ROW = 32 * TILES;  // bytes per token row
+  static constexpr int O_BYTES = BT * O_ROW;
+  static_assert(NCP == 0 || 2 * O_BYTES <= 32 * UTILE_BYTES, "o fits in the U tiles of the other parts");
 };
 
 // Copy round k of part p's share of a block (same offsets in LDS as in the
@@ -112,25 +114,40 @@ __device__ __forceinline__ void copy_step(const uint8_t *src, uint8_t *dst, int 
   }
 }
 
-// Touch a whole block, one dword per 128-byte line, from the NCP copy waves
-// (loads land in a junk LDS word per lane), so that the copy a chunk later
-// hits L2.  Every lane issues TOUCH_LOADS loads, so the number in flight is
-// known to the explicit waits.
-constexpr int TOUCH_LINES = (BLOCK_BYTES + 127) / 128;  // 612
-template <int NCP>
-struct Touch {
-  static constexpr int LOADS = NCP > 0 ? (TOUCH_LINES + 64 * NCP - 1) / (64 * NCP) : 1;
-  static_assert(LOADS < 16, "fits the low vmcnt field");
-  // s_waitcnt immediates (vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8])
-  static constexpr int WAIT_ALL_BUT_TOUCH = LOADS | (7 << 4);
+// Where the o of a chunk is staged: the U tiles of part p + 1.
+template <class C>
+__device__ __forceinline__ int o_stage_off(int p) {
+  return OFF_U + ((p + 1) % C::PARTS) * C::TILES * 2 * ROUND;
+}
+
+// Copy wave cw stores o of chunk c (staged in LDS buffer `buf` by the
+// compute waves) to its rows of o: 16 bytes per lane, through a buffer
+// resource that ends after the chunk's last valid row, so that the lanes of
+// rows past n are dropped by the range check and every store instruction is
+// issued (the copy waves count their outstanding stores exactly).
+template <class C, int NCP>
+struct OStore {
+  static constexpr int STORES = NCP > 0 ? C::O_BYTES / 16 / (64 * NCP) : 1;  // per copy wave and chunk
+  static_assert(STORES >= 1 && STORES < 16, "fits the low vmcnt field");
 };
-template <int NCP>
-__device__ __forceinline__ void touch_block(const uint8_t *src, uint8_t *junk_wave, int ct) {
+template <class C, int NCP>
+__device__ __forceinline__ void store_o_staged(const RecurArgs &a, const uint8_t *buf, int64_t c,
+                                               int h, int p, int cw, int l) {
+  const int4 info = chunk_record(a.chunk_info, c);
+  const int64_t t0 = info.x < 0 ? 0 : (info.x > a.T ? a.T : info.x);
+  const int n = (int)(info.y < 0 ? 0 : (info.y > a.T - t0 ? a.T - t0 : (info.y > BT ? BT : info.y)));
+  constexpr int PER_ROW = C::O_ROW / 16;  // 16-byte pieces per token row
+  const uint8_t *src = buf + o_stage_off<C>(p);
+  const int row_bytes = a.H * DV * 2;  // < 2^25: H <= 65535
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<bf16_t *>(a.o) + (t0 * a.H + h) * DV, 0, n * row_bytes, BUF_DWORD3);
 #pragma unroll
-  for (int k = 0; k < Touch<NCP>::LOADS; ++k) {
-    int line = ct + 64 * NCP * k;
-    line = line < TOUCH_LINES ? line : 0;
-    dma4(src + line * 128, junk_wave);
+  for (int k = 0; k < OStore<C, NCP>::STORES; ++k) {
+    const int i = (k * NCP + cw) * 64 + l;
+    const int row = i / PER_ROW, piece = i % PER_ROW;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(src + i * 16);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, row * row_bytes + 2 * (16 * C::TILES * p + 8 * piece),
+                                           0, CPOL_NT);
   }
 }
 
@@ -160,7 +177,6 @@ template <int NC, int NCP, int TPW>
 __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a) {
   using C = RecCfg<NC, NCP, TPW>;
   __shared__ __align__(16) uint8_t lds[2][BLOCK_BYTES];
-  __shared__ __align__(16) uint8_t junk[NCP > 0 ? NCP : 1][64 * 4];
   const int b = blockIdx.x;
   const int xcd = b & 7, i = b >> 3;
   const int64_t chain = (int64_t)(i / C::PARTS) * 8 + xcd;
@@ -180,27 +196,27 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
   const uint8_t *chain_blocks = a.blocks + (int64_t)h * nc_max * BLOCK_BYTES;
 
   if (NCP > 0 && w >= NC) {
-    // ---- copy waves: chunk c+1's block while chunk c is computed ----
-    // The chain's first part also touches the block two chunks ahead (the
-    // parts share one L2), leaving those loads in flight across the wait.
+    // ---- copy waves: chunk c+1's block while chunk c is computed, and
+    // the o of chunk c-1 (staged in LDS by the compute waves) to memory ----
+    // Each iteration issues the copy, then the stores; the wait at the top
+    // of the next one covers the copy but not the stores issued after it
+    // (vector memory operations complete in order).
     const int cw = w - NC;
-    const bool toucher = (p == 0);
     if (c_beg < c_end) copy_share<C, NCP>(chain_blocks + c_beg * BLOCK_BYTES, lds[0], cw, p, l);
-    if (toucher && c_beg + 1 < c_end)
-      touch_block<NCP>(chain_blocks + (c_beg + 1) * BLOCK_BYTES, junk[cw], cw * 64 + l);
-    bool touched = toucher && c_beg + 1 < c_end;
     for (int64_t c = c_beg; c < c_end; ++c) {
-      if (touched)
-        __builtin_amdgcn_s_waitcnt(Touch<NCP>::WAIT_ALL_BUT_TOUCH);
+      if (c > c_beg + 1)
+        __builtin_amdgcn_s_waitcnt(OStore<C, NCP>::STORES | (0x7 << 4));
       else
         __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      const int cur = (int)((c - c_beg) & 1);
       if (c + 1 < c_end)
-        copy_share<C, NCP>(chain_blocks + (c + 1) * BLOCK_BYTES, lds[(int)((c - c_beg) & 1) ^ 1], cw,
-                           p, l);
-      touched = toucher && c + 2 < c_end;
-      if (touched) touch_block<NCP>(chain_blocks + (c + 2) * BLOCK_BYTES, junk[cw], cw * 64 + l);
+        copy_share<C, NCP>(chain_blocks + (c + 1) * BLOCK_BYTES, lds[cur ^ 1], cw, p, l);
+      if (c > c_beg) store_o_staged<C, NCP>(a, lds[cur ^ 1], c - 1, h, p, cw, l);
     }
+    __syncthreads();  // the compute waves have staged the last chunk's o
+    if (c_end > c_beg)
+      store_o_staged<C, NCP>(a, lds[(int)((c_end - 1 - c_beg) & 1)], c_end - 1, h, p, cw, l);
     // no copy may still be writing LDS when the workgroup ends
     __builtin_amdgcn_s_waitcnt(0);
     return;
@@ -251,8 +267,12 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
   for (int64_t c = c_beg; c < c_end; ++c) {
     const int cur = (int)((c - c_beg) & 1);
     // after the barrier the copy waves' copies of this chunk are done, and
-    // nobody still reads the other buffer
-    __builtin_amdgcn_s_waitcnt(0);
+    // nobody still reads the other buffer (with copy waves, the compute
+    // waves' only memory accesses are LDS ones)
+    if (NCP > 0)
+      __builtin_amdgcn_s_waitcnt(LGKM_ONLY);
+    else
+      __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const uint8_t *blk = lds[cur];
     const int4 info = chunk_record(a.chunk_info, c);
@@ -310,7 +330,7 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
     for (int s4 = 0; s4 < 4; ++s4) {
       // one token tile of last chunk's o (and, without copy waves, a quarter
       // of the next chunk's copy)
-      if (c > c_beg) store_o_tile(s4);
+      if (NCP == 0 && c > c_beg) store_o_tile(s4);
       if (NCP == 0 && c + 1 < c_end)
         copy_step<C>(chain_blocks + (c + 1) * BLOCK_BYTES, lds[cur ^ 1], w, p, l, s4);
       bf16x8 nw[4], nq[4];
@@ -375,17 +395,31 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
         ot[lt_mt(x)][q] = mfma_bf16(vb[lt_s(x)][q], fal[x], ot[lt_mt(x)][q]);
       }
 
-    // o^T of this chunk as bf16 (nearest even), stored during the next one
+    // o^T of this chunk as bf16 (nearest even), stored during the next one:
+    // by the copy waves from LDS, or (without them) by this wave
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int q = 0; q < TPW; ++q)
 #pragma unroll
         for (int r = 0; r < 4; ++r) o_pend[mt][q][r] = (bf16_t)ot[mt][q][r];
+    if (NCP > 0) {
+      uint8_t *ost = lds[cur] + o_stage_off<C>(p);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int q = 0; q < TPW; ++q)
+          *reinterpret_cast<bf16x4 *>(ost + (16 * mt + nn) * C::O_ROW +
+                                      2 * (VCOL(nt0 + q, 4 * grp) - 16 * C::TILES * p)) =
+              o_pend[mt][q];
+    }
     o_t0 = t0;
     o_n = n;
   }
-  if (c_end > c_beg) {
+  if (NCP > 0) {
+    __builtin_amdgcn_s_waitcnt(LGKM_ONLY);
+    __syncthreads();  // the copy waves store the last chunk's o
+  } else if (c_end > c_beg) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) store_o_tile(mt);
   }
