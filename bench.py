@@ -32,7 +32,7 @@ METRIC = "KDA prefill tokens/s at T=8192,H=16,K=V=128 bf16; % MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, TFLOP/s
 MALL_BYTES = 256 * 2**20
-BLOCK_BYTES = 78336              # one (head, chunk) intermediate block
+BLOCK_BYTES = 72192              # one (head, chunk) intermediate block
 
 
 def parse():

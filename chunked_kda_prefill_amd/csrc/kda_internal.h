@@ -56,9 +56,8 @@ constexpr int CPOL_NT = 2;
 //   QG   : scale * q * Gamma, same shape and order as WN.
 //   KGT  : kg^T as A operand of S += kg^T v_new.  [key tile 0..7][token slab
 //          s 0..1]; lane slot e holds kg[P(s, grp, e)][16 mt + n].
-//   AQK  : Aqk as A operand of o += Aqk v_new, split in hi and lo bf16
-//          halves (hi fragments first).  Only the six (mt, s) fragments with
-//          any j <= i are stored, indexed by AQK_IDX.
+//   AQK  : Aqk as A operand of o += Aqk v_new (bf16).  Only the six
+//          (mt, s) fragments with any j <= i are stored, indexed by AQK_IDX.
 //   U    : U as the C-tile initialiser of v_new: [value tile nt 0..7][token
 //          tile pair 0..1] entries of 64 lanes x 16 bytes; bytes 8 m .. 8 m + 7
 //          of lane (n, grp) hold the C tile of token tile mt = 2 pair + m,
@@ -74,7 +73,7 @@ constexpr int OFF_QG = OFF_WN + 16 * FRAG_BYTES;
 constexpr int OFF_KGT = OFF_QG + 16 * FRAG_BYTES;
 constexpr int OFF_AQK = OFF_KGT + 16 * FRAG_BYTES;
 constexpr int AQK_FRAGS = 6;
-constexpr int OFF_U = OFF_AQK + 2 * AQK_FRAGS * FRAG_BYTES;
+constexpr int OFF_U = OFF_AQK + AQK_FRAGS * FRAG_BYTES;
 constexpr int UTILE_BYTES = 64 * 8;  // one value tile x token tile C tile (bf16)
 // byte offset of U's C tile (value tile nt, token tile mt) for lane l
 __host__ __device__ constexpr int U_OFFSET(int nt, int mt, int l) {

@@ -184,7 +184,11 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
   if (chain >= (int64_t)a.N * a.H) return;
   const int s = (int)(chain / a.H), h = (int)(chain % a.H);
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, nn = l & 15, grp = l >> 4;
+  // The wave index lives in a scalar register, so that every branch on a
+  // wave's role is a scalar jump.  MFMAs do not honour EXEC: under an
+  // exec-masked branch, a skipped path's MFMAs would still accumulate.
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, nn = l & 15, grp = l >> 4;
   const int nt0 = p * C::TILES + w * TPW;  // a compute wave's first value tile
   // chunk range and token ranges are clamped so that a workspace that does
   // not hold a valid chunk table can never send this kernel out of bounds
@@ -373,11 +377,10 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
         for (int e = 0; e < 8; ++e) vb[s2][q][e] = (bf16_t)vn[2 * s2 + (e >> 2)][q][e & 3];
 
     // h <- Diag(gamma) h + kg^T v_new   (the serial dependency: first)
-    bf16x8 fah[AQK_FRAGS], fal[AQK_FRAGS];
+    bf16x8 fa[AQK_FRAGS];
 #pragma unroll
     for (int x = 0; x < AQK_FRAGS; ++x) {
-      fah[x] = load_frag(blk + OFF_AQK + (x * 64 + l) * 16);
-      fal[x] = load_frag(blk + OFF_AQK + ((AQK_FRAGS + x) * 64 + l) * 16);
+      fa[x] = load_frag(blk + OFF_AQK + (x * 64 + l) * 16);
     }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
@@ -386,13 +389,12 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
 #pragma unroll
         for (int q = 0; q < TPW; ++q) S[t][q] = mfma_bf16(fk[s2][t], vb[s2][q], S[t][q]);
 
-    // o^T += v_new^T Aqk^T   (Aqk in hi + lo bf16)
+    // o^T += v_new^T Aqk^T
 #pragma unroll
     for (int x = 0; x < AQK_FRAGS; ++x)
 #pragma unroll
       for (int q = 0; q < TPW; ++q) {
-        ot[lt_mt(x)][q] = mfma_bf16(vb[lt_s(x)][q], fah[x], ot[lt_mt(x)][q]);
-        ot[lt_mt(x)][q] = mfma_bf16(vb[lt_s(x)][q], fal[x], ot[lt_mt(x)][q]);
+        ot[lt_mt(x)][q] = mfma_bf16(vb[lt_s(x)][q], fa[x], ot[lt_mt(x)][q]);
       }
 
     // o^T of this chunk as bf16 (nearest even), stored during the next one:

@@ -41,12 +41,12 @@ def test_workspace_size_and_layout():
     T, N, H = 8192, 4, 16
     lay = kda.workspace_layout(T, N, H)
     assert lay["nc_max"] == (T + 63 * N) // 64
-    assert lay["block_bytes"] == 78336
+    assert lay["block_bytes"] == 72192
     for key in ("chunk_first", "chunk_info", "blocks"):
         assert lay[key] % 256 == 0
     assert lay["chunk_info"] >= lay["chunk_first"] + 4 * (N + 1)
     assert lay["blocks"] >= lay["chunk_info"] + 16 * lay["nc_max"]
-    assert kda.workspace_size(T, N, H) == lay["blocks"] + H * lay["nc_max"] * 78336
+    assert kda.workspace_size(T, N, H) == lay["blocks"] + H * lay["nc_max"] * 72192
     assert kda.workspace_size(0, 1, 1) > 0
     for bad in [(-1, 1, 1), (10, 0, 1), (10, 1, 0)]:
         assert kda.workspace_size(*bad) == 0

@@ -187,5 +187,6 @@ def test_intra_intermediates(dev, lens, scale):
     # bf16 storage of one rounding: ~2^-9 relative per element
     for name in ("W", "U", "qg", "kg"):
         assert worst[name] < 4e-3, (name, worst[name])
-    assert worst["Aqk"] < 1e-4          # stored as hi + lo bf16
+    # Aqk: bf16 strip operands (one rounding each side), then bf16 storage
+    assert worst["Aqk"] < 8e-3
     assert worst["gamma"] < 1e-4

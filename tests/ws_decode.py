@@ -8,7 +8,7 @@ import numpy as np
 FRAG = 64 * 16
 OFF_WN, OFF_QG, OFF_KGT = 0, 16 * FRAG, 32 * FRAG
 OFF_AQK = 48 * FRAG
-OFF_U = OFF_AQK + 12 * FRAG
+OFF_U = OFF_AQK + 6 * FRAG
 OFF_GAM = OFF_U + 32 * 512
 BLOCK = OFF_GAM + 512
 LT_PAIRS = [(0, 0), (1, 0), (2, 0), (2, 1), (3, 0), (3, 1)]
@@ -56,12 +56,11 @@ def decode_block(raw: np.ndarray) -> dict:
                 for e in range(8):
                     KG[_perm_index(s, grp, e), 16 * mt + n] = fk[l, e]
     for x, (mt, s) in enumerate(LT_PAIRS):
-        hi = _frag(raw, OFF_AQK + x * FRAG)
-        lo = _frag(raw, OFF_AQK + (6 + x) * FRAG)
+        fa = _frag(raw, OFF_AQK + x * FRAG)
         for l in range(64):
             n, grp = l & 15, l >> 4
             for e in range(8):
-                AQK[16 * mt + n, _perm_index(s, grp, e)] = hi[l, e] + lo[l, e]
+                AQK[16 * mt + n, _perm_index(s, grp, e)] = fa[l, e]
     for nt in range(8):
         for mp in range(2):
             off = OFF_U + ((nt * 2 + mp) * 64) * 16
