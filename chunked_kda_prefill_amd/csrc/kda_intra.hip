@@ -88,7 +88,7 @@ __device__ __forceinline__ int lt_s(int x) { return (0x101000 >> (4 * x)) & 0xF;
 // the constant address space lets the compiler use scalar loads, which do
 // not wait on the kernel's own vector stores.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ int4 chunk_record(const int4 *info, int64_t c) {
+__device__ __forceinline__ int4 chunk_record(const int4 *info, int c) {
   const i32x4 v = ((const __attribute__((address_space(4))) i32x4 *)(uintptr_t)info)[c];
   return make_int4(v.x, v.y, v.z, v.w);
 }
@@ -99,7 +99,7 @@ __device__ __forceinline__ int32_t chunk_count(const int32_t *chunk_first, int N
 // Record of chunk c: from the workspace table, or (inline_table) computed
 // from the chunk offsets in LDS.  `s` is a running sequence index: the
 // chunks a workgroup visits only increase, so it only moves forward.
-__device__ __forceinline__ int4 unit_record(const IntraArgs &a, const int32_t *first_lds, int64_t c,
+__device__ __forceinline__ int4 unit_record(const IntraArgs &a, const int32_t *first_lds, int c,
                                             int &s) {
   if (!a.inline_table) return chunk_record(a.chunk_info, c);
   while (s + 1 < a.N && first_lds[s + 1] <= c) ++s;
@@ -265,9 +265,9 @@ __device__ __forceinline__ void load_v(const IntraArgs &a, int64_t t0, int n, in
 
 // One (chunk, head) unit whose inputs are already in `nxt` (loads issued).
 // After the unit's own inputs are consumed, `nxt` receives the next unit's.
-__device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, int64_t u,
-                                           int64_t units, UnitInputs &nxt, const int32_t *first_lds,
-                                           int &s_next) {
+__device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, int c, int h,
+                                           bool more, int cn, int hn, UnitInputs &nxt,
+                                           const int32_t *first_lds, int &s_next) {
   // threadIdx.x through an opaque move, so that address arithmetic derived
   // from it stays inside the unit loop instead of being hoisted out of it
   int tid;
@@ -278,12 +278,9 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, nn = l & 15, grp = l >> 4;
   const int row = SB * w + nn;
-  const int64_t c = u / a.H;
-  const int h = (int)(u % a.H);
   // the next unit's chunk record, fetched now so that its data loads can be
   // issued later without waiting on it
-  const int64_t un = u + gridDim.x;
-  const int4 info_next = unit_record(a, first_lds, (un < units ? un : u) / a.H, s_next);
+  const int4 info_next = unit_record(a, first_lds, more ? cn : c, s_next);
   UnitInputs in = nxt;
   const int n = in.n;
   uint2 qs[8], ks[8];  // q and k in the channel slots
@@ -443,7 +440,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
 
   // ---- the unit's q, k, g are consumed: start the next unit's loads (in
   // three parts, spread over the phases so no phase issues a burst) ----
-  if (un < units) load_unit(a, info_next, (int)(un % a.H), row, grp, nxt, 0);
+  if (more) load_unit(a, info_next, hn, row, grp, nxt, 0);
 
   // ---- off-diagonal strip blocks, two at most per wave:
   //   wave 0: (3,0)   wave 1: (1,0) (3,1)   wave 2: (2,0) (2,1)   wave 3: (3,2)
@@ -500,7 +497,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   }
   __syncthreads();
 
-  if (un < units) load_unit(a, info_next, (int)(un % a.H), row, grp, nxt, 1);
+  if (more) load_unit(a, info_next, hn, row, grp, nxt, 1);
 
   // ---- this unit's V (only U needs it, at the end) ----
   u32x4 vrow[4];
@@ -552,7 +549,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   }
   __syncthreads();
 
-  if (un < units) load_unit(a, info_next, (int)(un % a.H), row, grp, nxt, 2);
+  if (more) load_unit(a, info_next, hn, row, grp, nxt, 2);
 
   // ---- column w of T below the diagonal, top-down:
   // T_ab = -T_aa sum_{c=b}^{a-1} L_ac T_cb  with b = w, a = w + o ----
@@ -734,26 +731,42 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void in
     nc = chunk_count(a.chunk_first, a.N);
   }
   nc = nc < 0 ? 0 : (nc > a.nc_max ? a.nc_max : nc);
-  const int64_t units = nc * a.H;
-  int64_t u = blockIdx.x;
+  // units = nc * H <= nc_max * H <= INT32_MAX (checked on the host)
+  const int units = (int)(nc * a.H);
+  int u = blockIdx.x;
   if (u >= units) return;
   const int tid = threadIdx.x;
+  // (chunk, head) of the unit, stepped by the grid size without divisions
+  const int G = gridDim.x;
+  const int dc = G / a.H, dh = G % a.H;
+  int c = u / a.H, h = u % a.H;
   // running sequence index: the last sequence whose first chunk is at or
   // before this workgroup's first chunk (binary search once)
   int s_next = 0;
   if (a.inline_table) {
-    const int64_t c0 = u / a.H;
     int lo = 0, hi = a.N - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (first_lds[mid] <= c0) lo = mid; else hi = mid - 1;
+      if (first_lds[mid] <= c) lo = mid; else hi = mid - 1;
     }
     s_next = lo;
   }
   UnitInputs nxt;
-  load_unit(a, unit_record(a, first_lds, u / a.H, s_next), (int)(u % a.H),
-            SB * (tid >> 6) + (tid & 15), (tid >> 4) & 3, nxt);
-  for (; u < units; u += gridDim.x) intra_unit(a, sm, u, units, nxt, first_lds, s_next);
+  load_unit(a, unit_record(a, first_lds, c, s_next), h, SB * (tid >> 6) + (tid & 15),
+            (tid >> 4) & 3, nxt);
+  for (;;) {
+    const bool more = units - u > G;
+    int cn = c + dc, hn = h + dh;
+    if (hn >= a.H) {
+      hn -= a.H;
+      ++cn;
+    }
+    intra_unit(a, sm, c, h, more, cn, hn, nxt, first_lds, s_next);
+    if (!more) break;
+    u += G;
+    c = cn;
+    h = hn;
+  }
 }
 
 hipError_t launch_intra(const IntraArgs &a, hipStream_t stream) {
