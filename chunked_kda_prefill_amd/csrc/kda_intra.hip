@@ -170,13 +170,14 @@ constexpr int AUX_G = 0, AUX_QK = 0, AUX_V = CPOL_NT;
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-// Buffer over rows [tb, tb + 64) of a [T, H, 128] tensor (clamped to T).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_rsrc(const void *base, int64_t tb, int64_t T,
+// Buffer over the unit's n valid rows (starting at row tb) of head h of a
+// [T, H, 128] tensor.  A lane whose row is past n addresses beyond the
+// record count, so the hardware range check returns zeros for it: rows past
+// a partial chunk's end load as q = k = v = g = beta = 0 with no masking.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_rsrc(const void *base, int64_t tb, int n,
                                                              int H, int h, int elem) {
-  const int64_t rows = T - tb < BT ? T - tb : BT;
   const char *p = static_cast<const char *>(base) + ((tb * H + h) * DK) * elem;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), 0, (int)(rows * H * DK * elem),
-                                           BUF_DWORD3);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), 0, n * H * DK * elem, BUF_DWORD3);
 }
 
 // bf16 rows are read 16 bytes per lane: for key slab s (32 channels) lane
@@ -203,9 +204,8 @@ struct UnitInputs {
   float beta;
 };
 
-// Issues the loads; rows past n are read from an in-bounds row (so every
-// lane loads, back to back, without branches) and zeroed where they are
-// used, through row_mask().
+// Issues the loads (every lane loads, back to back, without branches; rows
+// past n read as zeros, see unit_rsrc).
 __device__ __forceinline__ void load_unit(const IntraArgs &a, const int4 info, int h, int row,
                                           int grp, UnitInputs &in, int part = -1) {
   // the chunk table is written by the same call; clamping keeps even a
@@ -213,29 +213,28 @@ __device__ __forceinline__ void load_unit(const IntraArgs &a, const int4 info, i
   const int64_t t0 = info.x < 0 ? 0 : (info.x > a.T ? a.T : info.x);
   const int n = (int)(info.y < 0 ? 0 : (info.y > a.T - t0 ? a.T - t0 : (info.y > BT ? BT : info.y)));
   const int64_t tb = t0 < a.T ? t0 : a.T - 1;  // first row of the unit's buffers
-  const int r = row < n ? row : 0;               // row within them
-  const int roff = r * a.H * DK;                 // < 2^23 elements: H <= 65535
+  const int roff = row * a.H * DK;               // < 2^23 elements: H <= 65535
   if (part <= 0) {
     in.t0 = t0;
     in.n = n;
-    const __amdgpu_buffer_rsrc_t rg = unit_rsrc(a.g, tb, a.T, a.H, h, 4);
+    const __amdgpu_buffer_rsrc_t rg = unit_rsrc(a.g, tb, n, a.H, h, 4);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       in.g[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
                                                rg, 4 * (roff + slot_ch(j, grp)), 0, AUX_G));
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(a.beta + tb * a.H + h), 0, (int)((a.T - tb) * a.H * 4), BUF_DWORD3);
-    in.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * r * a.H, 0, AUX_G));
+        const_cast<float *>(a.beta + tb * a.H + h), 0, n * a.H * 4, BUF_DWORD3);
+    in.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * row * a.H, 0, AUX_G));
   }
   if (part < 0 || part == 1) {
-    const __amdgpu_buffer_rsrc_t rq = unit_rsrc(a.q, tb, a.T, a.H, h, 2);
+    const __amdgpu_buffer_rsrc_t rq = unit_rsrc(a.q, tb, n, a.H, h, 2);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       in.q[s] = __builtin_amdgcn_raw_buffer_load_b128(rq, 2 * (roff + 32 * s + 8 * load_m(grp)), 0,
                                                       AUX_QK);
   }
   if (part < 0 || part == 2) {
-    const __amdgpu_buffer_rsrc_t rk = unit_rsrc(a.k, tb, a.T, a.H, h, 2);
+    const __amdgpu_buffer_rsrc_t rk = unit_rsrc(a.k, tb, n, a.H, h, 2);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       in.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rk, 2 * (roff + 32 * s + 8 * load_m(grp)), 0,
@@ -243,12 +242,6 @@ __device__ __forceinline__ void load_unit(const IntraArgs &a, const int4 info, i
   }
 }
 
-__device__ __forceinline__ uint32_t row_mask(int row, int n) { return row < n ? 0xffffffffu : 0u; }
-__device__ __forceinline__ uint2 masked(uint2 x, uint32_t m) { return make_uint2(x.x & m, x.y & m); }
-__device__ __forceinline__ float4 masked(float4 x, uint32_t m) {
-  return make_float4(__uint_as_float(__float_as_uint(x.x) & m), __uint_as_float(__float_as_uint(x.y) & m),
-                     __uint_as_float(__float_as_uint(x.z) & m), __uint_as_float(__float_as_uint(x.w) & m));
-}
 
 // V rows of the lane (needed only for U, so loaded late), 16 bytes per
 // key slab: channels 32 s + 8 load_m(grp) + 0..7.  Rows past n are zeroed
@@ -256,8 +249,8 @@ __device__ __forceinline__ float4 masked(float4 x, uint32_t m) {
 __device__ __forceinline__ void load_v(const IntraArgs &a, int64_t t0, int n, int h, int row,
                                        int grp, u32x4 (&v)[4]) {
   const int64_t tb = t0 < a.T ? t0 : a.T - 1;
-  const int roff = (row < n ? row : 0) * a.H * DK;
-  const __amdgpu_buffer_rsrc_t rv = unit_rsrc(a.v, tb, a.T, a.H, h, 2);
+  const int roff = row * a.H * DK;
+  const __amdgpu_buffer_rsrc_t rv = unit_rsrc(a.v, tb, n, a.H, h, 2);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
     v[s] = __builtin_amdgcn_raw_buffer_load_b128(rv, 2 * (roff + 32 * s + 8 * load_m(grp)), 0, AUX_V);
@@ -291,14 +284,13 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   }
   uint8_t *blk = a.blocks + ((int64_t)h * a.nc_max + c) * BLOCK_BYTES;
   float *rt = sm.tt;  // [0, 4 DK): reference rows; [4 DK, 8 DK): subblock totals
-  const uint32_t rmask = row_mask(row, n);
 
   // ---- subblock cumsum down the wave's 16 rows; publish the reference row
   // and the total of each subblock.  (The previous unit last read tt, beta
   // and tab before its last barrier, so these writes are safe.) ----
   float4 G[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) G[j] = subblock_scan(masked(in.g[j], rmask));
+  for (int j = 0; j < 8; ++j) G[j] = subblock_scan(in.g[j]);
   if (nn == SB_REF) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) *reinterpret_cast<float4 *>(&rt[w * DK + slot_ch(j, grp)]) = G[j];
@@ -308,7 +300,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
     for (int j = 0; j < 8; ++j)
       *reinterpret_cast<float4 *>(&rt[(4 + w) * DK + slot_ch(j, grp)]) = G[j];
   }
-  if (grp == 0) sm.beta[row] = row < n ? in.beta : 0.f;
+  if (grp == 0) sm.beta[row] = in.beta;
   __syncthreads();
 
   // ---- per-channel tables (two threads per channel) ----
@@ -359,8 +351,8 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
       const float qv[4] = {Q.x, Q.y, Q.z, Q.w};
       const float d[4] = {G[j].x - r7.x, G[j].y - r7.y, G[j].z - r7.z, G[j].w - r7.w};
       float qf[4], kf[4], kgv[4], kmv[4], ktv[4];
-      unpack4(masked(qs[j], rmask), qf);
-      unpack4(masked(ks[j], rmask), kf);
+      unpack4(qs[j], qf);
+      unpack4(ks[j], kf);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float t = d[e] * LOG2E;
@@ -629,7 +621,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   bf16_t *vt = kgt;
 #pragma unroll
   for (int s = 0; s < 4; ++s)
-    *reinterpret_cast<u32x4 *>(&vt[sw_bf16(row, 32 * s + 8 * load_m(grp))]) = vrow[s] & rmask;
+    *reinterpret_cast<u32x4 *>(&vt[sw_bf16(row, 32 * s + 8 * load_m(grp))]) = vrow[s];
   __syncthreads();
 
   auto th = [&](int x) { return *reinterpret_cast<const bf16x8 *>(&tfr[(x * 64 + l) * 8]); };
