@@ -42,20 +42,34 @@ __device__ __forceinline__ bf16x8 load_frag(const uint8_t *p) {
   return *reinterpret_cast<const bf16x8 *>(p);
 }
 
-// One global_load_lds_dwordx4: 16 bytes per lane from src into LDS at
-// lds_wave_base + 16 * lane.  Written as inline assembly so that the
-// compiler does not treat it as an LDS store it must wait for before every
-// later LDS read (it cannot tell the two block buffers apart); the kernel
-// waits for these copies itself, at the top of each chunk.
+// One buffer_load_dwordx4 ... lds: 16 bytes per lane from byte off + 16 lane
+// of a block (buffer resource r, voff = 16 lane) into LDS at lds_base + off +
+// 16 lane.  The block offset travels in a scalar register and the LDS
+// address in M0, so a round costs three instructions.  Written as inline
+// assembly so that the compiler does not treat it as an LDS store it must
+// wait for before every later LDS read (it cannot tell the two block buffers
+// apart); the kernel waits for these copies itself, once per chunk.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
-__device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *lds_wave_base) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+__device__ __forceinline__ void dma_round(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t off,
+                                          uint32_t lds_base) {
+  // both scalars are wave-uniform; readfirstlane keeps them in SGPRs where
+  // the compiler cannot prove it
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base + off);
+  const uint32_t soff = __builtin_amdgcn_readfirstlane(off);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
                :
-               : "v"(src), "s"(base)
+               : "v"(voff), "s"(r), "s"(m0v), "s"(soff)
                : "memory", "m0");
+}
+// Buffer resource over one intermediate block, and the wave-uniform LDS
+// address of a block buffer.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t *blk) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(blk), 0, BLOCK_BYTES, BUF_DWORD3);
+}
+__device__ __forceinline__ uint32_t lds_base_of(const uint8_t *buf) {
+  return __builtin_amdgcn_readfirstlane(lds_addr(buf));
 }
 
 // s_waitcnt immediate that waits for LDS (and scalar) accesses only:
@@ -89,7 +103,8 @@ struct RecCfg {
 // Copy round k of part p's share of a block (same offsets in LDS as in the
 // block): shared rounds, then the part's U tiles, then gamma (lanes < 32).
 template <class C>
-__device__ __forceinline__ void copy_round(const uint8_t *src, uint8_t *dst, int k, int p, int l) {
+__device__ __forceinline__ void copy_round(__amdgpu_buffer_rsrc_t r, uint32_t lbase, int k, int p,
+                                           int l) {
   int off;
   if (k < SHARED_ROUNDS)
     off = k * ROUND;
@@ -97,7 +112,7 @@ __device__ __forceinline__ void copy_round(const uint8_t *src, uint8_t *dst, int
     off = OFF_U + (p * C::U_ROUNDS + (k - SHARED_ROUNDS)) * ROUND;
   else
     off = OFF_GAM;
-  if (k < C::ROUNDS - 1 || l < DK * 4 / 16) dma16(src + off + l * 16, dst + off);
+  if (k < C::ROUNDS - 1 || l < DK * 4 / 16) dma_round(r, 16 * l, off, lbase);
 }
 
 // Without copy waves: compute wave w copies rounds w, w + NC, ..., a
@@ -107,10 +122,12 @@ __device__ __forceinline__ void copy_step(const uint8_t *src, uint8_t *dst, int 
                                           int step) {
   constexpr int per_wave = (C::ROUNDS + C::NCW - 1) / C::NCW;
   constexpr int per_step = (per_wave + 3) / 4;
+  const __amdgpu_buffer_rsrc_t r = block_rsrc(src);
+  const uint32_t lbase = lds_base_of(dst);
 #pragma unroll
   for (int j = step * per_step; j < (step + 1) * per_step && j < per_wave; ++j) {
     const int k = w + C::NCW * j;
-    if (k < C::ROUNDS) copy_round<C>(src, dst, k, p, l);
+    if (k < C::ROUNDS) copy_round<C>(r, lbase, k, p, l);
   }
 }
 
@@ -151,14 +168,25 @@ __device__ __forceinline__ void store_o_staged(const RecurArgs &a, const uint8_t
   }
 }
 
-// Copy wave cw's share of part p's block: rounds cw, cw + NCP, ...
+// Rounds [K0, K1) of part p's share, with compile-time offsets.
+template <class C, int K0, int K1>
+__device__ __forceinline__ void copy_range(__amdgpu_buffer_rsrc_t r, uint32_t lbase, int p, int l) {
+#pragma unroll
+  for (int k = K0; k < K1; ++k) copy_round<C>(r, lbase, k, p, l);
+}
+
+// Copy wave cw's share of part p's block: the first or the second half of
+// the rounds (two copy waves per workgroup).
 template <class C, int NCP>
 __device__ __forceinline__ void copy_share(const uint8_t *src, uint8_t *dst, int cw, int p, int l) {
-#pragma unroll
-  for (int k0 = 0; k0 < C::ROUNDS; k0 += NCP) {
-    const int k = k0 + cw;
-    if (k < C::ROUNDS) copy_round<C>(src, dst, k, p, l);
-  }
+  static_assert(NCP == 0 || NCP == 2, "the copy is split between two copy waves");
+  constexpr int HALF = (C::ROUNDS + 1) / 2;
+  const __amdgpu_buffer_rsrc_t r = block_rsrc(src);
+  const uint32_t lbase = lds_base_of(dst);
+  if (cw == 0)
+    copy_range<C, 0, HALF>(r, lbase, p, l);
+  else
+    copy_range<C, HALF, C::ROUNDS>(r, lbase, p, l);
 }
 
 }  // namespace
@@ -172,7 +200,7 @@ __device__ __forceinline__ void copy_share(const uint8_t *src, uint8_t *dst, int
 // read from HBM once and hit in L2 by the other parts.  The chain's
 // intermediate blocks stream through two LDS buffers: while the waves compute
 // chunk c from one buffer, chunk c+1's block is copied global -> LDS into
-// the other by global_load_lds_dwordx4 (no register staging).
+// the other by buffer_load_dwordx4 ... lds (no register staging).
 template <int NC, int NCP, int TPW>
 __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a) {
   using C = RecCfg<NC, NCP, TPW>;
