@@ -274,14 +274,13 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   // the next unit's chunk record, fetched now so that its data loads can be
   // issued later without waiting on it
   const int4 info_next = unit_record(a, first_lds, more ? cn : c, s_next);
-  UnitInputs in = nxt;
+  // The unit's inputs are read in place: each part of `nxt` is consumed
+  // before the next unit's loads into that part are issued (g and beta in
+  // the cumsum phase, q and k in the factor phase), so no register copy of
+  // the inputs waits for all their loads at once.
+  const UnitInputs &in = nxt;
   const int n = in.n;
-  uint2 qs[8], ks[8];  // q and k in the channel slots
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    slab_to_slots(in.q[s], qs[2 * s], qs[2 * s + 1]);
-    slab_to_slots(in.k[s], ks[2 * s], ks[2 * s + 1]);
-  }
+  const int64_t t0 = in.t0;
   uint8_t *blk = a.blocks + ((int64_t)h * a.nc_max + c) * BLOCK_BYTES;
   float *rt = sm.tt;  // [0, 4 DK): reference rows; [4 DK, 8 DK): subblock totals
 
@@ -334,6 +333,13 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   // Aqk^T block (w, b): lane holds [j = 16b + 4grp + r][i = 16w + nn]; it is
   // half (b & 1) of the recurrence's Aqk fragment (mt = w, s = b >> 1).
   // L block (w, b): lane holds [i = 16w + 4grp + r][j = 16b + nn] * beta_i.
+  // q and k in the channel slots (their loads are waited for here)
+  uint2 qs[8], ks[8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    slab_to_slots(in.q[s], qs[2 * s], qs[2 * s + 1]);
+    slab_to_slots(in.k[s], ks[2 * s], ks[2 * s + 1]);
+  }
   uint2 kgb[8], kgm[8];
   bf16x8 qh[4], kh[4];
   f32x4 accA = zero4(), accL = zero4();
@@ -493,7 +499,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
 
   // ---- this unit's V (only U needs it, at the end) ----
   u32x4 vrow[4];
-  load_v(a, in.t0, in.n, h, row, grp, vrow);
+  load_v(a, t0, n, h, row, grp, vrow);
 
   // ---- kg and K*Gamma rows into bf16 tiles where k~ was ----
   bf16_t *kgt = reinterpret_cast<bf16_t *>(sm.x);
