@@ -56,7 +56,7 @@ def test_headline(dev):
     parity(o, f, *run_oracle(w), "headline")
 
 
-@pytest.mark.parametrize("B", [1, 8, 64])
+@pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32, 64])
 def test_batch(dev, B):
     w = wl.batch(B)
     heads = [0, 7, 15]
