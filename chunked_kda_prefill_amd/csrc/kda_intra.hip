@@ -120,11 +120,17 @@ struct __align__(16) IntraSmem {
 static_assert(sizeof(IntraSmem) + 4 * (INLINE_SEQS + 1) <= 80 * 1024, "two units fit one CU's LDS");
 static_assert(sizeof(TableScratch) <= sizeof(float) * BT * DK, "table scratch fits where k~ goes");
 
-__device__ __forceinline__ void store_bf16x4(uint8_t *p, const bf16x4 &x) {
-  *reinterpret_cast<bf16x4 *>(p) = x;
+// Block stores go through a buffer resource over the unit's block: the
+// fragment offset is a scalar operand and the lane offset a fixed VGPR, so
+// no 64-bit address is formed per store.
+typedef unsigned u32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_bf16x4(__amdgpu_buffer_rsrc_t r, int off, int voff,
+                                             const bf16x4 &x) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2v, x), r, voff, off, 0);
 }
-__device__ __forceinline__ void store_bf16x8(uint8_t *p, const bf16x8 &x) {
-  *reinterpret_cast<bf16x8 *>(p) = x;
+__device__ __forceinline__ void store_bf16x8(__amdgpu_buffer_rsrc_t r, int off, int voff,
+                                             const bf16x8 &x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, off, 0);
 }
 
 __device__ __forceinline__ void unpack4(uint2 u, float (&f)[4]) {
@@ -282,6 +288,8 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   const int n = in.n;
   const int64_t t0 = in.t0;
   uint8_t *blk = a.blocks + ((int64_t)h * a.nc_max + c) * BLOCK_BYTES;
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(blk, 0, BLOCK_BYTES, BUF_DWORD3);
+  const int lv16 = 16 * l;  // lane offset of a fragment store
   float *rt = sm.tt;  // [0, 4 DK): reference rows; [4 DK, 8 DK): subblock totals
 
   // ---- subblock cumsum down the wave's 16 rows; publish the reference row
@@ -378,7 +386,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
       pin(kgb[j]);
       *reinterpret_cast<float4 *>(&sm.x[sw_f32(row, ch)]) = make_float4(ktv[0], ktv[1], ktv[2], ktv[3]);
     }
-    store_bf16x8(blk + OFF_QG + ((w * 4 + s) * 64 + l) * 16, f);
+    store_bf16x8(br, OFF_QG + (w * 4 + s) * FRAG_BYTES, lv16, f);
     pin(qh[s]);
     pin(kh[s]);
     accA = mfma_bf16(kth, qh[s], accA);
@@ -389,7 +397,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   }
   if (w == 0) {
     const float2 gv = *reinterpret_cast<const float2 *>(&sm.tab[TAB_GAM][2 * l]);
-    *reinterpret_cast<float2 *>(blk + OFF_GAM + 8 * l) = gv;
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2v, gv), br, 8 * l, OFF_GAM, 0);
   }
 
   // Epilogue of strip block (ba, bb): Aqk^T half to the block, L (times
@@ -408,9 +416,9 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
     const int idx = AQK_IDX(ba, bb >> 1), half = bb & 1;
     if (zero_upper) {
       const bf16_t z = (bf16_t)0.f;
-      store_bf16x8(blk + OFF_AQK + (idx * 64 + l) * 16, bf16x8{ah[0], ah[1], ah[2], ah[3], z, z, z, z});
+      store_bf16x8(br, OFF_AQK + idx * FRAG_BYTES, lv16, bf16x8{ah[0], ah[1], ah[2], ah[3], z, z, z, z});
     } else {
-      store_bf16x4(blk + OFF_AQK + (idx * 64 + l) * 16 + half * 8, ah);
+      store_bf16x4(br, OFF_AQK + idx * FRAG_BYTES + half * 8, lv16, ah);
     }
     const f32x4 bv = as_f32x4(*reinterpret_cast<const float4 *>(&sm.beta[SB * ba + 4 * grp]));
 #pragma unroll
@@ -602,7 +610,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
       fr[e] = lo4[e];
       fr[4 + e] = hi4[e];
     }
-    store_bf16x8(blk + OFF_KGT + ((mtc * 2 + s) * 64 + l) * 16, fr);
+    store_bf16x8(br, OFF_KGT + (mtc * 2 + s) * FRAG_BYTES, lv16, fr);
   }
   __syncthreads();
 
@@ -667,7 +675,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
 #pragma unroll
         for (int r = 0; r < 4; ++r) uv[4 * m + r] = (bf16_t)acc[r];
       }
-      store_bf16x8(blk + U_OFFSET(nt, 2 * mp, l), uv);
+      store_bf16x8(br, U_OFFSET(nt, 2 * mp, 0), lv16, uv);
     }  }
 
   // ---- W^T = (K*Gamma)^T T'^T: wave w owns key tiles 2w and 2w+1, which
@@ -705,7 +713,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
 #pragma unroll
         for (int r = 0; r < 4; ++r) wv[4 * q2 + r] = (bf16_t)(-acc[r]);
       }
-      store_bf16x8(blk + OFF_WN + ((nti * 4 + w) * 64 + l) * 16, wv);
+      store_bf16x8(br, OFF_WN + (nti * 4 + w) * FRAG_BYTES, lv16, wv);
     }
   }
 }
