@@ -197,6 +197,36 @@ def test_intra_then_recurrence_equals_fwd(dev):
     assert torch.equal(f1, f2)
 
 
+def test_workspace_contents_do_not_matter(dev):
+    # The workspace is scratch: whatever it holds on entry (zeros, all ones,
+    # random bytes, an earlier call's table and intermediates), the outputs
+    # are bitwise those of a fresh workspace, and the flags word reports no
+    # malformed input.  Full-size (4 x 2048 tokens x 16 heads, several units
+    # per workgroup of the intra-chunk kernel).
+    import torch
+    import chunked_kda_prefill_amd as kda
+    w = wl.headline()
+    log("[case] workspace contents on entry")
+    o_ref, f_ref = run_gpu(w, dev)
+    parity(o_ref[:, [5]], f_ref[:, [5]], *run_oracle(w, heads=[5]), "headline head 5")
+    t = wl.to_torch(w, dev)
+    ws = kda.new_workspace(w.T, w.N, w.H, dev)
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    fills = [("zeros", lambda: ws.zero_()),
+             ("ones", lambda: ws.fill_(0xFF)),
+             ("random", lambda: ws.copy_(torch.randint(0, 256, ws.shape, generator=gen,
+                                                      dtype=torch.uint8).to(dev))),
+             ("as left", lambda: None)]
+    for name, fill in fills:
+        fill()
+        o, f = kda.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
+                             initial_state=t["initial_state"], scale=w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32).item()) == 0, name
+        assert np.array_equal(wl.bf16_tensor_to_f32(o).astype(np.float64), o_ref), name
+        assert np.array_equal(f.cpu().numpy().astype(np.float64), f_ref), name
+
+
 @pytest.mark.parametrize("gmul", [0.0, 0.01], ids=["g_zero", "weak_decay"])
 def test_weak_and_no_decay(dev, gmul):
     # with little or no decay the state carries the whole history, the
