@@ -761,6 +761,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void in
   load_unit(a, unit_record(a, first_lds, c, s_next), h, SB * (tid >> 6) + (tid & 15),
             (tid >> 4) & 3, nxt);
   for (;;) {
+    // Issue priority = units left (capped at 3): of the two workgroups on a
+    // CU the one behind gets picked first, so both end together instead of
+    // the younger one (the arbiter otherwise prefers older waves) running its
+    // last unit alone.
+    const int left = (units - 1 - u) / G + 1;
+    if (left >= 3)
+      __builtin_amdgcn_s_setprio(3);
+    else if (left == 2)
+      __builtin_amdgcn_s_setprio(2);
+    else
+      __builtin_amdgcn_s_setprio(1);
     const bool more = units - u > G;
     int cn = c + dc, hn = h + dh;
     if (hn >= a.H) {
