@@ -56,14 +56,23 @@ namespace {
 constexpr int NT = CHUNK_THREADS;  // 4 waves
 constexpr float LOG2E = 1.4426950408889634f;
 
-// Row-major [64][128] tiles with their 16-byte chunks XOR-swizzled by the row
-// (chunk' = chunk ^ (row & 7)), so that the 16-byte fragment reads of 8
-// consecutive rows hit different LDS banks.
+// Row-major [64][128] tiles with their 16-byte chunks XOR-swizzled by the
+// row.  The LDS has 64 four-byte banks and serves a 16-byte-per-lane access
+// 16 lanes (256 bytes) at a time, an 8-byte one 32 lanes at a time; the XOR
+// spreads the rows those groups touch over all 64 banks.  fp32 tiles (32
+// chunks per row): chunk ^ (row & 15), for the 16 rows of a lane group.  bf16
+// tiles (16 chunks per row): chunk ^ s(row & 15) with s(r) = r ^ 12 (r & 1);
+// besides the 16 rows of a row-wise write, this also separates the 4
+// consecutive rows times 2 or 4 neighbouring chunks that the transposed
+// fragment reads take per 16 lanes (the reads of V, whose value columns are
+// interleaved for the recurrence's output tiles, stay at two cycles per
+// 256 bytes).
 __device__ __forceinline__ int sw_bf16(int row, int ch) {  // bf16 element index
-  return row * DK + ((((ch >> 3) ^ (row & 7)) << 3) | (ch & 7));
+  const int r = row & 15;
+  return row * DK + ((((ch >> 3) ^ r ^ (12 * (r & 1))) << 3) | (ch & 7));
 }
 __device__ __forceinline__ int sw_f32(int row, int ch) {  // fp32 element index
-  return row * DK + ((((ch >> 2) ^ (row & 7)) << 2) | (ch & 3));
+  return row * DK + ((((ch >> 2) ^ (row & 15)) << 2) | (ch & 3));
 }
 // The 64 x 64 fp32 L and T: 16-byte chunks swizzled by (row & 15), so the
 // 16 rows an MFMA operand read touches land in different banks.
