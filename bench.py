@@ -54,6 +54,8 @@ def parse():
                     help="repeat the oracle sample until it has used this much CPU time")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a plain device copy of this size first (counter scale)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline line: per-config latency table (markdown)")
     return ap.parse_args()
 
 
@@ -79,6 +81,81 @@ def measured_traffic(workload: str, kernel: str):
     return int(round((k["fetch_kib"] * rec["fetch_factor"] + k["write_kib"] * rec["write_factor"]) * 1024))
 
 
+SWEEP_CONFIGS = ["tiny", "headline"] + [f"batch{b}" for b in (1, 2, 4, 8, 16, 32, 64)] + \
+    ["sharegpt", "long"]
+
+
+def sweep(args, torch, np, kda, wl):
+    """Per-config latency of one kda_chunk_fwd call on cold inputs: 20 warmup
+    calls, then 100 calls, each after an untimed read of a 512 MiB device
+    buffer that evicts L2 and the MALL (a read, so that no dirty lines are
+    left to write back during the call), bracketed by HIP events on the
+    call's stream.
+    Prints a markdown table: median / p10 / p90, tokens/s, algorithmic GB/s
+    and TFLOP/s, the fraction of 8 TB/s, and the fp64 oracle's rate on a
+    bounded sample (a few heads) of the same inputs."""
+    import oracle
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.ones(128 * 2**20, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    # achievable ceiling: a plain device copy of 1 GiB
+    a = torch.ones(2**28, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 10 * 2 * a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    threads = oracle.max_threads()
+    print(f"Device copy of 1 GiB (read + write): {copy_gbs:.0f} GB/s "
+          f"({copy_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s). Oracle threads: {threads}.\n")
+    print("| config | T | N | H | chunks | median µs | p10 µs | p90 µs | M tokens/s | GB/s | "
+          "HBM frac | TFLOP/s | oracle tokens/s (heads) | GPU/oracle |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for name in SWEEP_CONFIGS:
+        w = wl.by_name(name)
+        T, N, H = w.T, w.N, w.H
+        t = wl.to_torch(w, dev)
+        ws = kda.new_workspace(T, N, H, dev)
+        o = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+        fin = torch.empty((N, H, 128, 128), dtype=torch.float32, device=dev)
+        call = lambda: kda.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
+                                     initial_state=t["initial_state"], scale=w.scale, workspace=ws,
+                                     o=o, final_state=fin)
+        for _ in range(20):
+            call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(100)]
+        for i, (x, y) in enumerate(evs):
+            torch.sum(flush, dim=0, out=sink)
+            x.record(stream)
+            call()
+            y.record(stream)
+        torch.cuda.synchronize()
+        us = np.array([x.elapsed_time(y) * 1e3 for x, y in evs])
+        med, p10, p90 = (float(np.percentile(us, q)) for q in (50, 10, 90))
+        nbytes, flops = wl.algorithmic_bytes(w), wl.algorithmic_flops(w)
+        gbs = nbytes / (med * 1e-6) / 1e9
+        # oracle on a bounded sample: at most 2 heads (tokens/s scaled to all)
+        hs = list(range(min(H, 2)))
+        c0 = time.perf_counter()
+        oracle.kda_fwd(w.q, w.k, w.v, w.g, w.beta, w.cu_seqlens, w.initial_state,
+                       scale=w.scale, heads=hs)
+        cw = time.perf_counter() - c0
+        otps = T * len(hs) / H / cw
+        print(f"| {w.name} | {T} | {N} | {H} | {w.num_chunks()} | {med:.1f} | {p10:.1f} | "
+              f"{p90:.1f} | {T / med:.2f} | {gbs:.0f} | {gbs / HBM_PEAK_GBS:.3f} | "
+              f"{flops / (med * 1e-6) / 1e12:.1f} | {otps:,.0f} ({len(hs)}) | "
+              f"{(T / (med * 1e-6)) / otps:,.0f}x |", flush=True)
+        del t, ws, o, fin
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -93,6 +170,9 @@ def main():
 
     import chunked_kda_prefill_amd as kda
     from chunked_kda_prefill_amd import workloads as wl
+    if args.sweep:
+        sweep(args, torch, np, kda, wl)
+        return
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
