@@ -82,7 +82,7 @@ def measured_traffic(workload: str, kernel: str):
 
 
 SWEEP_CONFIGS = ["tiny", "headline"] + [f"batch{b}" for b in (1, 2, 4, 8, 16, 32, 64)] + \
-    ["sharegpt", "long"]
+    ["sharegpt", "long", "decode16x1_h12", "decode16x4_h12", "decode64x1_h16", "decode64x1_h96"]
 
 
 def sweep(args, torch, np, kda, wl):
@@ -118,16 +118,23 @@ def sweep(args, torch, np, kda, wl):
     print("| config | T | N | H | chunks | median µs | p10 µs | p90 µs | M tokens/s | GB/s | "
           "HBM frac | TFLOP/s | oracle tokens/s (heads) | GPU/oracle |")
     print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
-    for name in SWEEP_CONFIGS:
+    runs = [r for n in SWEEP_CONFIGS for r in
+            ([(n, "decode_fwd"), (n, "chunk_fwd")] if n.startswith("decode") else [(n, "chunk_fwd")])]
+    for name, entry in runs:
         w = wl.by_name(name)
         T, N, H = w.T, w.N, w.H
         t = wl.to_torch(w, dev)
         ws = kda.new_workspace(T, N, H, dev)
         o = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
         fin = torch.empty((N, H, 128, 128), dtype=torch.float32, device=dev)
-        call = lambda: kda.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
-                                     initial_state=t["initial_state"], scale=w.scale, workspace=ws,
-                                     o=o, final_state=fin)
+        if entry == "decode_fwd":
+            call = lambda: kda.decode_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                          t["cu_seqlens"], initial_state=t["initial_state"],
+                                          scale=w.scale, o=o, final_state=fin)
+        else:
+            call = lambda: kda.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                         t["cu_seqlens"], initial_state=t["initial_state"],
+                                         scale=w.scale, workspace=ws, o=o, final_state=fin)
         for _ in range(20):
             call()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -149,7 +156,8 @@ def sweep(args, torch, np, kda, wl):
                        scale=w.scale, heads=hs)
         cw = time.perf_counter() - c0
         otps = T * len(hs) / H / cw
-        print(f"| {w.name} | {T} | {N} | {H} | {w.num_chunks()} | {med:.1f} | {p10:.1f} | "
+        label = w.name if entry == "chunk_fwd" else f"{w.name} (kda_decode_fwd)"
+        print(f"| {label} | {T} | {N} | {H} | {w.num_chunks()} | {med:.1f} | {p10:.1f} | "
               f"{p90:.1f} | {T / med:.2f} | {gbs:.0f} | {gbs / HBM_PEAK_GBS:.3f} | "
               f"{flops / (med * 1e-6) / 1e12:.1f} | {otps:,.0f} ({len(hs)}) | "
               f"{(T / (med * 1e-6)) / otps:,.0f}x |", flush=True)

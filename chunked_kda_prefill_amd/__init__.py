@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     chunk_intra,
     chunk_recurrence,
     chunk_table,
+    decode_fwd,
     gate_cumsum,
     load_library,
     new_workspace,

@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPOR
 # Every symbol include/kda.h declares.
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
             "kda_chunk_table", "kda_gate_cumsum", "kda_chunk_intra",
-            "kda_workspace_layout", "kda_chunk_recurrence")
+            "kda_workspace_layout", "kda_chunk_recurrence", "kda_decode_fwd")
 
 
 class KDAError(RuntimeError):
@@ -55,6 +55,8 @@ def load_library():
     lib.kda_chunk_fwd_workspace_size.restype = SZ
     lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F32, P, P, P, SZ, P]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_decode_fwd.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F32, P, P, P]
+    lib.kda_decode_fwd.restype = ctypes.c_int
     lib.kda_chunk_table.argtypes = [P, I64, I32, P, P, P, P]
     lib.kda_chunk_table.restype = ctypes.c_int
     lib.kda_gate_cumsum.argtypes = [P, P, I64, I32, I32, P, P, SZ, P]
@@ -175,6 +177,34 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, scale: Optional[
         T, N, H, float(scale), _ptr(o), _ptr(final_state), _ptr(workspace),
         workspace.numel(), _stream(dev))
     _check("kda_chunk_fwd", st)
+    return o, final_state
+
+
+def decode_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, scale: Optional[float] = None,
+               output_final_state: bool = True, o=None, final_state=None) -> Tuple[object, object]:
+    """Token-serial KDA forward for decode steps and speculative verification
+    windows (kda_decode_fwd): the same arguments and results as chunk_fwd,
+    without a workspace; meant for a few tokens per sequence.  Pass
+    final_state=initial_state to update the state in place."""
+    torch = _torch()
+    T, N, H = _check_inputs(q, k, v, g, beta, cu_seqlens)
+    dev = q.device
+    if initial_state is not None:
+        _expect(initial_state, "initial_state", torch.float32, (N, H, HEAD_DIM, HEAD_DIM))
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    if o is None:
+        o = torch.empty((T, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    else:
+        _expect(o, "o", torch.bfloat16, (T, H, HEAD_DIM))
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, HEAD_DIM, HEAD_DIM), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _expect(final_state, "final_state", torch.float32, (N, H, HEAD_DIM, HEAD_DIM))
+    st = load_library().kda_decode_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+        T, N, H, float(scale), _ptr(o), _ptr(final_state), _stream(dev))
+    _check("kda_decode_fwd", st)
     return o, final_state
 
 

@@ -232,6 +232,37 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
   return run_recurrence(initial_state, T, N, H, o, final_state, ws, stream);
 }
 
+kda_status kda_decode_fwd(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                          int64_t T, int32_t N, int32_t H, float scale, void *o,
+                          float *final_state, hipStream_t stream) {
+  kda_status st = check_sizes(T, N, H);
+  if (st != KDA_OK) return st;
+  if ((int64_t)N * H * 2 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+  if ((st = check_inputs(q, k, v, g, beta, cu_seqlens, T)) != KDA_OK) return st;
+  if ((st = check_outputs(initial_state, T, N, H, o, final_state)) != KDA_OK) return st;
+  const int64_t tok = T * H * DK;
+  if (overlap(o, tok * 2, q, tok * 2) || overlap(o, tok * 2, k, tok * 2) ||
+      overlap(o, tok * 2, v, tok * 2) || overlap(o, tok * 2, g, tok * 4) ||
+      overlap(o, tok * 2, beta, T * H * 4))
+    return KDA_ERR_INVALID_ARGUMENT;
+  DecodeArgs da;
+  da.q = static_cast<const uint16_t *>(q);
+  da.k = static_cast<const uint16_t *>(k);
+  da.v = static_cast<const uint16_t *>(v);
+  da.g = g;
+  da.beta = beta;
+  da.cu = cu_seqlens;
+  da.h0 = initial_state;
+  da.hT = final_state;
+  da.o = static_cast<uint16_t *>(o);
+  da.T = T;
+  da.N = N;
+  da.H = H;
+  da.scale = scale;
+  return hip_status(launch_decode(da, stream));
+}
+
 kda_status kda_chunk_recurrence(const float *initial_state, int64_t T, int32_t N, int32_t H,
                                 void *o, float *final_state, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream) {

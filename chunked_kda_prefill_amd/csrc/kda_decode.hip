@@ -1,0 +1,120 @@
+// Token-serial KDA step for decode and speculative verification (MI355X
+// Kimi K3 post, section 1.2: one fused kernel per decode step that keeps the
+// recurrent state on chip while it applies a sequence's new tokens; section
+// 1.3: 16 users, 1 token each or a 4-token verification window).
+//
+// Per (sequence, head), for each of the sequence's tokens t in order, with
+// S the fp32 state [128 keys][128 values]:
+//     S   <- Diag(exp g_t) S
+//     S   <- S + beta_t k_t (v_t - S^T k_t)^T
+//     o_t  = scale S^T q_t                     (reads the updated state)
+// which is the gated delta rule the chunked prefill computes in chunk form.
+// With few tokens per sequence the work is the state's read and write (128
+// KiB per (sequence, head)), so the kernel streams the state once and keeps
+// it in registers across the tokens.
+//
+// Work split.  The 128 value columns evolve independently, so a workgroup
+// owns 64 of them for one (sequence, head): lane l of wave w holds column
+// v0 + l and key rows 32 w .. 32 w + 31 (32 registers).  Both reductions over
+// the keys (S^T k and S^T q) are a per-lane sum over its 32 rows, then the
+// four waves' partial sums added in LDS in a fixed order, so results are
+// deterministic.  State loads and stores are 256-byte row segments per wave.
+#include "kda_internal.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int DEC_COLS = 64;               // value columns per workgroup
+constexpr int DEC_WAVES = 4;               // key rows split over the waves
+constexpr int DEC_ROWS = DK / DEC_WAVES;   // key rows per wave
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(DecodeArgs a) {
+  __shared__ float ks[DK], qs[DK], eg[DK];
+  __shared__ float red[DEC_WAVES][DEC_COLS];
+  const int64_t wg = blockIdx.x;
+  const int half = (int)(wg % (DV / DEC_COLS));
+  const int64_t sh = wg / (DV / DEC_COLS);
+  const int h = (int)(sh % a.H);
+  const int s = (int)(sh / a.H);
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int col = half * DEC_COLS + l;
+  const int r0 = w * DEC_ROWS;
+  const int64_t st_base = ((int64_t)s * a.H + h) * DK * DV;
+
+  // the sequence's tokens, with cu_seqlens clamped into [0, T] (malformed
+  // offsets never send the kernel out of bounds)
+  int64_t t_beg = a.cu[s], t_end = a.cu[s + 1];
+  t_beg = t_beg < 0 ? 0 : (t_beg > a.T ? a.T : t_beg);
+  t_end = t_end < t_beg ? t_beg : (t_end > a.T ? a.T : t_end);
+
+  float S[DEC_ROWS];
+#pragma unroll
+  for (int r = 0; r < DEC_ROWS; ++r)
+    S[r] = a.h0 ? a.h0[st_base + (int64_t)(r0 + r) * DV + col] : 0.f;
+
+  for (int64_t t = t_beg; t < t_end; ++t) {
+    const int64_t tok = (t * a.H + h) * DK;
+    if (tid < DK) {
+      ks[tid] = bf16_to_f32(a.k[tok + tid]);
+      eg[tid] = expf(a.g[tok + tid]);
+    } else {
+      qs[tid - DK] = bf16_to_f32(a.q[tok + tid - DK]);
+    }
+    const float vv = bf16_to_f32(a.v[tok + col]);
+    const float beta = a.beta[t * a.H + h];
+    __syncthreads();
+
+    // decay, then this wave's part of (S^T k)[col]
+    float pu = 0.f;
+#pragma unroll
+    for (int r = 0; r < DEC_ROWS; ++r) {
+      S[r] *= eg[r0 + r];
+      pu = fmaf(S[r], ks[r0 + r], pu);
+    }
+    red[w][l] = pu;
+    __syncthreads();
+    const float u = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
+    const float d = beta * (vv - u);
+
+    // rank-one write, then this wave's part of (S^T q)[col]
+    float po = 0.f;
+#pragma unroll
+    for (int r = 0; r < DEC_ROWS; ++r) {
+      S[r] = fmaf(ks[r0 + r], d, S[r]);
+      po = fmaf(S[r], qs[r0 + r], po);
+    }
+    __syncthreads();  // every wave has read red (u) and ks, qs, eg
+    red[w][l] = po;
+    __syncthreads();
+    if (w == 0) {
+      const float o = a.scale * (((red[0][l] + red[1][l]) + red[2][l]) + red[3][l]);
+      a.o[tok + col] = __builtin_bit_cast(uint16_t, (__bf16)o);  // nearest even
+    }
+    // the next token's staging writes come after wave 0 has read red: it
+    // reaches the next barrier only after that read
+  }
+
+  if (a.hT) {
+#pragma unroll
+    for (int r = 0; r < DEC_ROWS; ++r) a.hT[st_base + (int64_t)(r0 + r) * DV + col] = S[r];
+  }
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  const int64_t wgs = (int64_t)a.N * a.H * (DV / DEC_COLS);
+  if (wgs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_kernel, dim3((unsigned)wgs), dim3(64 * DEC_WAVES), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace kda

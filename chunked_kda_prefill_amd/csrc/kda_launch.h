@@ -45,4 +45,18 @@ struct RecurArgs {
 };
 hipError_t launch_recurrence(const RecurArgs &a, hipStream_t stream);
 
+struct DecodeArgs {
+  const uint16_t *q, *k, *v;  // bf16 bits [T, H, 128]
+  const float *g;             // [T, H, 128]
+  const float *beta;          // [T, H]
+  const int32_t *cu;          // cu_seqlens [N + 1]
+  const float *h0;            // [N, H, 128, 128] or null
+  float *hT;                  // [N, H, 128, 128] or null
+  uint16_t *o;                // bf16 bits [T, H, 128]
+  int64_t T;
+  int32_t N, H;
+  float scale;
+};
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
 }  // namespace kda

@@ -195,6 +195,13 @@ def long_single() -> Workload:
                          h0="normal", pinned_fraction=0.10)
 
 
+def decode_step(users: int, tokens: int, H: int) -> Workload:
+    """A decode step (tokens = 1) or a speculative-verification window
+    (tokens = 4) for `users` sequences with cached states, ~N(0, 0.1)."""
+    return make_workload(f"decode_{users}x{tokens}_H{H}", [tokens] * users, H=H,
+                         seed=200 + 10 * tokens + users % 10, h0="normal")
+
+
 def small(lengths, H: int = 2, seed: int = 7, h0: str = "normal",
           pinned_fraction: float = 0.0, scale: Optional[float] = None) -> Workload:
     """A small ad-hoc workload for parity and edge-case tests."""
@@ -214,6 +221,10 @@ def by_name(name: str) -> Workload:
         return sharegpt_like()
     if name == "long":
         return long_single()
+    if name.startswith("decode"):  # decodeUxT_hH, e.g. decode16x1_h12
+        ut, hh = name[len("decode"):].split("_h")
+        u, t = ut.split("x")
+        return decode_step(int(u), int(t), int(hh))
     raise ValueError(f"unknown workload {name!r}")
 
 

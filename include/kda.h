@@ -102,6 +102,30 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
                          hipStream_t stream);
 
 /*
+ * Token-serial KDA forward for decode and speculative verification (MI355X
+ * Kimi K3 post, sections 1.2-1.3: one fused kernel applies each sequence's
+ * new tokens, 1 for a decode step or a window of a few for verification,
+ * to its recurrent state, which stays on chip).  For every sequence s and
+ * head h, and each token t of the sequence in order:
+ *     S <- Diag(exp g_t) S;  S <- S + beta_t k_t (v_t - S^T k_t)^T;
+ *     o_t = scale S^T q_t.
+ * This is the same function kda_chunk_fwd computes, evaluated token by token
+ * in fp32 (the two differ only by rounding).  Any sequence length is
+ * accepted, but the cost grows with the longest sequence, so it is meant
+ * for a handful of tokens per sequence; prefill belongs to kda_chunk_fwd.
+ *
+ * Arguments, layouts, aliasing and errors are those of kda_chunk_fwd
+ * (initial_state NULL means zeros; final_state NULL is not written and may
+ * alias initial_state exactly).  It needs no workspace and enqueues one
+ * kernel on `stream`.  KDA_ERR_UNSUPPORTED if N * H * 2 exceeds 2^31 - 1.
+ */
+kda_status kda_decode_fwd(const void *q, const void *k, const void *v,
+                          const float *g, const float *beta,
+                          const float *initial_state, const int32_t *cu_seqlens,
+                          int64_t T, int32_t N, int32_t H, float scale,
+                          void *o, float *final_state, hipStream_t stream);
+
+/*
  * Step-level entry points.  They run the steps of kda_chunk_fwd on their
  * own so that each step can be checked and timed separately; kda_chunk_fwd
  * does not call them.

@@ -104,6 +104,28 @@ def test_step_entry_points_reject_bad_arguments():
     assert lib.kda_workspace_layout(-5, 1, 1, out) == 1
 
 
+def test_decode_entry_rejects_bad_arguments():
+    # host-checked argument errors of kda_decode_fwd (no launch is reached)
+    lib = kda.load_library()
+    A = 1 << 20
+    def dec(**over):
+        a = dict(q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, h0=None, cu=6 * A, T=128, N=1,
+                 H=2, scale=1.0, o=7 * A, hT=8 * A, stream=None)
+        a.update(over)
+        return lib.kda_decode_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"], a["cu"],
+                                  a["T"], a["N"], a["H"], a["scale"], a["o"], a["hT"], a["stream"])
+    INV, UNS = 1, 2
+    assert dec(q=None) == INV
+    assert dec(cu=None) == INV
+    assert dec(o=None) == INV
+    assert dec(T=-1) == INV
+    assert dec(N=0) == INV
+    assert dec(H=70000) == UNS
+    assert dec(k=(2 << 20) + 8) == INV                     # misaligned
+    assert dec(o=(3 << 20) + 64) == INV                    # o aliases v
+    assert dec(h0=8 << 20, hT=(8 << 20) + 256) == INV     # partly overlapping states
+
+
 def test_python_wrapper_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "_lib", None)
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
