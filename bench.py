@@ -83,6 +83,9 @@ def measured_traffic(workload: str, kernel: str):
 
 SWEEP_CONFIGS = ["tiny", "headline"] + [f"batch{b}" for b in (1, 2, 4, 8, 16, 32, 64)] + \
     ["sharegpt", "long", "decode16x1_h12", "decode16x4_h12", "decode64x1_h16", "decode64x1_h96"]
+# configs also timed through the fused-prologue entry points, and with the
+# same prologue done by separate torch ops in front of the plain entry point
+FUSED_SWEEP_CONFIGS = ("headline", "long", "decode16x4_h12", "decode64x1_h96")
 
 
 def sweep(args, torch, np, kda, wl):
@@ -93,7 +96,10 @@ def sweep(args, torch, np, kda, wl):
     call's stream.
     Prints a markdown table: median / p10 / p90, tokens/s, algorithmic GB/s
     and TFLOP/s, the fraction of 8 TB/s, and the fp64 oracle's rate on a
-    bounded sample (a few heads) of the same inputs."""
+    bounded sample (a few heads) of the same inputs.  Decode configs are
+    also timed through kda_decode_fwd; the FUSED_SWEEP_CONFIGS also through
+    the fused-prologue entry points (raw q, k and strided bf16 beta logits),
+    and with that prologue done by torch ops before the plain entry point."""
     import oracle
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
@@ -118,8 +124,12 @@ def sweep(args, torch, np, kda, wl):
     print("| config | T | N | H | chunks | median µs | p10 µs | p90 µs | M tokens/s | GB/s | "
           "HBM frac | TFLOP/s | oracle tokens/s (heads) | GPU/oracle |")
     print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
-    runs = [r for n in SWEEP_CONFIGS for r in
-            ([(n, "decode_fwd"), (n, "chunk_fwd")] if n.startswith("decode") else [(n, "chunk_fwd")])]
+    runs = []
+    for n in SWEEP_CONFIGS:
+        main = ["decode_fwd", "chunk_fwd"] if n.startswith("decode") else ["chunk_fwd"]
+        if n in FUSED_SWEEP_CONFIGS:
+            main = main + [e + "_fused" for e in main] + ["torch prologue + " + main[0]]
+        runs += [(n, e) for e in main]
     for name, entry in runs:
         w = wl.by_name(name)
         T, N, H = w.T, w.N, w.H
@@ -127,14 +137,35 @@ def sweep(args, torch, np, kda, wl):
         ws = kda.new_workspace(T, N, H, dev)
         o = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
         fin = torch.empty((N, H, 128, 128), dtype=torch.float32, device=dev)
-        if entry == "decode_fwd":
-            call = lambda: kda.decode_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"],
-                                          t["cu_seqlens"], initial_state=t["initial_state"],
-                                          scale=w.scale, o=o, final_state=fin)
+        fused = "fused" in entry or "prologue" in entry
+        if fused:
+            # raw q, k and bf16 beta logits in a strided [T, 5 + H + 3] slice
+            rq, rk, bfull, pre = wl.raw_prologue_inputs(w, 300)
+            bf = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(
+                dev).view(torch.bfloat16)
+            t["q"], t["k"], blog = bf(rq), bf(rk), bf(bfull)[:, pre:pre + H]
+        is_dec = entry.split(" + ")[-1].startswith("decode_fwd")
+        plain = kda.decode_fwd if is_dec else kda.chunk_fwd
+        extra = {} if is_dec else {"workspace": ws}
+        if entry.endswith("_fused"):
+            fn = kda.decode_fwd_fused if entry == "decode_fwd_fused" else kda.chunk_fwd_fused
+            call = lambda: fn(t["q"], t["k"], t["v"], t["g"], blog, t["cu_seqlens"],
+                              initial_state=t["initial_state"], scale=w.scale, qk_eps=1e-6,
+                              o=o, final_state=fin, **extra)
+        elif fused:
+            def call():
+                beta = torch.sigmoid(blog.float())
+                qn = (t["q"].float() * torch.rsqrt((t["q"].float() ** 2).sum(-1, keepdim=True)
+                                                   + 1e-6)).to(torch.bfloat16)
+                kn = (t["k"].float() * torch.rsqrt((t["k"].float() ** 2).sum(-1, keepdim=True)
+                                                   + 1e-6)).to(torch.bfloat16)
+                plain(qn, kn, t["v"], t["g"], beta, t["cu_seqlens"],
+                      initial_state=t["initial_state"], scale=w.scale, o=o, final_state=fin,
+                      **extra)
         else:
-            call = lambda: kda.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"],
-                                         t["cu_seqlens"], initial_state=t["initial_state"],
-                                         scale=w.scale, workspace=ws, o=o, final_state=fin)
+            call = lambda: plain(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
+                                 initial_state=t["initial_state"], scale=w.scale, o=o,
+                                 final_state=fin, **extra)
         for _ in range(20):
             call()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -156,12 +187,14 @@ def sweep(args, torch, np, kda, wl):
                        scale=w.scale, heads=hs)
         cw = time.perf_counter() - c0
         otps = T * len(hs) / H / cw
-        label = w.name if entry == "chunk_fwd" else f"{w.name} (kda_decode_fwd)"
+        label = w.name if entry == "chunk_fwd" else f"{w.name} ({entry.replace('_fwd', '')})"
         print(f"| {label} | {T} | {N} | {H} | {w.num_chunks()} | {med:.1f} | {p10:.1f} | "
               f"{p90:.1f} | {T / med:.2f} | {gbs:.0f} | {gbs / HBM_PEAK_GBS:.3f} | "
               f"{flops / (med * 1e-6) / 1e12:.1f} | {otps:,.0f} ({len(hs)}) | "
               f"{(T / (med * 1e-6)) / otps:,.0f}x |", flush=True)
         del t, ws, o, fin
+        if fused:
+            del blog
 
 
 def main():

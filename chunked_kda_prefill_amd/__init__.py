@@ -10,10 +10,12 @@ from ._binding import (  # noqa: F401
     KDAError,
     LIB_PATH,
     chunk_fwd,
+    chunk_fwd_fused,
     chunk_intra,
     chunk_recurrence,
     chunk_table,
     decode_fwd,
+    decode_fwd_fused,
     gate_cumsum,
     load_library,
     new_workspace,

@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPOR
 # Every symbol include/kda.h declares.
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
             "kda_chunk_table", "kda_gate_cumsum", "kda_chunk_intra",
-            "kda_workspace_layout", "kda_chunk_recurrence", "kda_decode_fwd")
+            "kda_workspace_layout", "kda_chunk_recurrence", "kda_decode_fwd",
+            "kda_chunk_fwd_fused", "kda_decode_fwd_fused")
 
 
 class KDAError(RuntimeError):
@@ -57,6 +58,11 @@ def load_library():
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_decode_fwd.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F32, P, P, P]
     lib.kda_decode_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_fused.argtypes = [P, P, P, P, P, I64, F32, P, P, I64, I32, I32, F32, P, P, P,
+                                        SZ, P]
+    lib.kda_chunk_fwd_fused.restype = ctypes.c_int
+    lib.kda_decode_fwd_fused.argtypes = [P, P, P, P, P, I64, F32, P, P, I64, I32, I32, F32, P, P, P]
+    lib.kda_decode_fwd_fused.restype = ctypes.c_int
     lib.kda_chunk_table.argtypes = [P, I64, I32, P, P, P, P]
     lib.kda_chunk_table.restype = ctypes.c_int
     lib.kda_gate_cumsum.argtypes = [P, P, I64, I32, I32, P, P, SZ, P]
@@ -129,7 +135,8 @@ def _check_inputs(q, k, v, g, beta, cu_seqlens):
     _expect(k, "k", torch.bfloat16, (T, H, HEAD_DIM))
     _expect(v, "v", torch.bfloat16, (T, H, HEAD_DIM))
     _expect(g, "g", torch.float32, (T, H, HEAD_DIM))
-    _expect(beta, "beta", torch.float32, (T, H))
+    if beta is not None:
+        _expect(beta, "beta", torch.float32, (T, H))
     _expect(cu_seqlens, "cu_seqlens", torch.int32)
     if cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 2:
         raise ValueError("cu_seqlens must be [N + 1] with N >= 1")
@@ -205,6 +212,76 @@ def decode_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, scale: Optional
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
         T, N, H, float(scale), _ptr(o), _ptr(final_state), _stream(dev))
     _check("kda_decode_fwd", st)
+    return o, final_state
+
+
+def _fused_outputs(q, cu_seqlens, initial_state, o, final_state, output_final_state, T, N, H):
+    torch = _torch()
+    dev = q.device
+    if initial_state is not None:
+        _expect(initial_state, "initial_state", torch.float32, (N, H, HEAD_DIM, HEAD_DIM))
+    if o is None:
+        o = torch.empty((T, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    else:
+        _expect(o, "o", torch.bfloat16, (T, H, HEAD_DIM))
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, HEAD_DIM, HEAD_DIM), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _expect(final_state, "final_state", torch.float32, (N, H, HEAD_DIM, HEAD_DIM))
+    return o, final_state
+
+
+def _beta_logits(b, T: int, H: int):
+    """b: a bf16 [T, W] tensor or a column slice of one (W >= H); returns its
+    row stride in elements."""
+    torch = _torch()
+    if b.dtype != torch.bfloat16 or b.dim() != 2 or b.shape[0] != T or b.shape[1] != H \
+            or b.stride(1) != 1 or (T > 1 and b.stride(0) < H):
+        raise ValueError("b must be a bf16 [T, H] tensor with unit column stride (a column "
+                         "slice of a row-major projection output is fine)")
+    return int(b.stride(0)) if T > 1 else H
+
+
+def chunk_fwd_fused(q, k, v, g, b, cu_seqlens, initial_state=None, scale: Optional[float] = None,
+                    qk_eps: Optional[float] = 1e-6, output_final_state: bool = True,
+                    workspace=None, o=None, final_state=None):
+    """chunk_fwd with the prologue fused in (kda_chunk_fwd_fused): beta =
+    sigmoid(b) from bf16 logits b [T, H] (a strided column slice is fine),
+    and, unless qk_eps is None, q and k L2-normalised per (token, head) as
+    x / sqrt(sum x^2 + qk_eps)."""
+    T, N, H = _check_inputs(q, k, v, g, None, cu_seqlens)
+    stride = _beta_logits(b, T, H)
+    o, final_state = _fused_outputs(q, cu_seqlens, initial_state, o, final_state,
+                                    output_final_state, T, N, H)
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    if workspace is None:
+        workspace = new_workspace(T, N, H, q.device)
+    st = load_library().kda_chunk_fwd_fused(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), stride,
+        -1.0 if qk_eps is None else float(qk_eps), _ptr(initial_state), _ptr(cu_seqlens),
+        T, N, H, float(scale), _ptr(o), _ptr(final_state), _ptr(workspace), workspace.numel(),
+        _stream(q.device))
+    _check("kda_chunk_fwd_fused", st)
+    return o, final_state
+
+
+def decode_fwd_fused(q, k, v, g, b, cu_seqlens, initial_state=None, scale: Optional[float] = None,
+                     qk_eps: Optional[float] = 1e-6, output_final_state: bool = True, o=None,
+                     final_state=None):
+    """decode_fwd with the prologue fused in (kda_decode_fwd_fused); b and
+    qk_eps as in chunk_fwd_fused."""
+    T, N, H = _check_inputs(q, k, v, g, None, cu_seqlens)
+    stride = _beta_logits(b, T, H)
+    o, final_state = _fused_outputs(q, cu_seqlens, initial_state, o, final_state,
+                                    output_final_state, T, N, H)
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    st = load_library().kda_decode_fwd_fused(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), stride,
+        -1.0 if qk_eps is None else float(qk_eps), _ptr(initial_state), _ptr(cu_seqlens),
+        T, N, H, float(scale), _ptr(o), _ptr(final_state), _stream(q.device))
+    _check("kda_decode_fwd_fused", st)
     return o, final_state
 
 

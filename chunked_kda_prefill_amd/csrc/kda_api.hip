@@ -55,13 +55,19 @@ kda_status carve(void *workspace, size_t workspace_bytes, int64_t T, int32_t N, 
 }
 
 kda_status check_inputs(const void *q, const void *k, const void *v, const float *g,
-                        const float *beta, const int32_t *cu, int64_t T) {
+                        const float *beta, const int32_t *cu, int64_t T,
+                        const void *b = nullptr, int64_t b_stride = 0, int32_t H = 0) {
   if (!cu || !aligned(cu, 4)) return KDA_ERR_INVALID_ARGUMENT;
   if (T > 0) {
-    if (!q || !k || !v || !g || !beta) return KDA_ERR_INVALID_ARGUMENT;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) ||
-        !aligned(beta, 4))
+    if (!q || !k || !v || !g) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16))
       return KDA_ERR_INVALID_ARGUMENT;
+    if (b) {  // beta logits of a strided slice
+      if (!aligned(b, 2) || b_stride < H || b_stride > (int64_t(1) << 24))
+        return KDA_ERR_INVALID_ARGUMENT;
+    } else if (!beta || !aligned(beta, 4)) {
+      return KDA_ERR_INVALID_ARGUMENT;
+    }
   }
   return KDA_OK;
 }
@@ -162,9 +168,19 @@ static kda_status run_recurrence(const float *initial_state, int64_t T, int32_t 
   return hip_status(launch_recurrence(ra, stream));
 }
 
+// Fused prologue options of an entry point: beta from bf16 logits b with
+// row stride b_stride (b null: beta as given), and q, k L2-normalised with
+// qk_eps when qk_eps >= 0.
+struct Prologue {
+  const uint16_t *b = nullptr;
+  int64_t b_stride = 0;
+  float qk_eps = -1.f;
+};
+
 static kda_status run_intra(const void *q, const void *k, const void *v, const float *g,
                             const float *beta, const int32_t *cu_seqlens, int64_t T, int32_t N,
-                            int32_t H, float scale, const Ws &ws, hipStream_t stream) {
+                            int32_t H, float scale, const Ws &ws, hipStream_t stream,
+                            const Prologue &pro = Prologue()) {
   // small batches: the intra-chunk kernel builds the chunk table itself (one
   // launch less); larger ones get the standalone table kernel first
   const bool inline_table = N <= INLINE_SEQS && ws.L.nc_max > 0;
@@ -190,6 +206,9 @@ static kda_status run_intra(const void *q, const void *k, const void *v, const f
   ia.H = H;
   ia.scale = scale;
   ia.inline_table = inline_table ? 1 : 0;
+  ia.b = pro.b;
+  ia.b_stride = pro.b_stride;
+  ia.qk_eps = pro.qk_eps;
   return hip_status(launch_intra(ia, stream));
 }
 
@@ -205,21 +224,23 @@ kda_status kda_chunk_intra(const void *q, const void *k, const void *v, const fl
   return run_intra(q, k, v, g, beta, cu_seqlens, T, N, H, scale, ws, stream);
 }
 
-kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
-                         const float *beta, const float *initial_state, const int32_t *cu_seqlens,
-                         int64_t T, int32_t N, int32_t H, float scale, void *o,
-                         float *final_state, void *workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *initial_state,
+                                 const int32_t *cu_seqlens, int64_t T, int32_t N, int32_t H,
+                                 float scale, void *o, float *final_state, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream, const Prologue &pro) {
   kda_status st = check_sizes(T, N, H);
   if (st != KDA_OK) return st;
-  if ((st = check_inputs(q, k, v, g, beta, cu_seqlens, T)) != KDA_OK) return st;
+  if ((st = check_inputs(q, k, v, g, beta, cu_seqlens, T, pro.b, pro.b_stride, H)) != KDA_OK)
+    return st;
   if ((st = check_outputs(initial_state, T, N, H, o, final_state)) != KDA_OK) return st;
   const int64_t tok = T * H * DK;
   const int64_t st_bytes = (int64_t)N * H * DK * DV * 4;
   // o must not alias any input
   if (overlap(o, tok * 2, q, tok * 2) || overlap(o, tok * 2, k, tok * 2) ||
       overlap(o, tok * 2, v, tok * 2) || overlap(o, tok * 2, g, tok * 4) ||
-      overlap(o, tok * 2, beta, T * H * 4))
+      overlap(o, tok * 2, beta, T * H * 4) ||
+      (pro.b && overlap(o, tok * 2, pro.b, ((T - 1) * pro.b_stride + H) * 2)))
     return KDA_ERR_INVALID_ARGUMENT;
   Ws ws;
   if ((st = carve(workspace, workspace_bytes, T, N, H, ws)) != KDA_OK) return st;
@@ -227,24 +248,27 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
       overlap(workspace, ws.L.total, final_state, st_bytes))
     return KDA_ERR_INVALID_ARGUMENT;
 
-  if ((st = run_intra(q, k, v, g, beta, cu_seqlens, T, N, H, scale, ws, stream)) != KDA_OK)
+  if ((st = run_intra(q, k, v, g, beta, cu_seqlens, T, N, H, scale, ws, stream, pro)) != KDA_OK)
     return st;
   return run_recurrence(initial_state, T, N, H, o, final_state, ws, stream);
 }
 
-kda_status kda_decode_fwd(const void *q, const void *k, const void *v, const float *g,
-                          const float *beta, const float *initial_state, const int32_t *cu_seqlens,
-                          int64_t T, int32_t N, int32_t H, float scale, void *o,
-                          float *final_state, hipStream_t stream) {
+static kda_status decode_fwd_impl(const void *q, const void *k, const void *v, const float *g,
+                                  const float *beta, const float *initial_state,
+                                  const int32_t *cu_seqlens, int64_t T, int32_t N, int32_t H,
+                                  float scale, void *o, float *final_state, hipStream_t stream,
+                                  const Prologue &pro) {
   kda_status st = check_sizes(T, N, H);
   if (st != KDA_OK) return st;
   if ((int64_t)N * H * 2 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
-  if ((st = check_inputs(q, k, v, g, beta, cu_seqlens, T)) != KDA_OK) return st;
+  if ((st = check_inputs(q, k, v, g, beta, cu_seqlens, T, pro.b, pro.b_stride, H)) != KDA_OK)
+    return st;
   if ((st = check_outputs(initial_state, T, N, H, o, final_state)) != KDA_OK) return st;
   const int64_t tok = T * H * DK;
   if (overlap(o, tok * 2, q, tok * 2) || overlap(o, tok * 2, k, tok * 2) ||
       overlap(o, tok * 2, v, tok * 2) || overlap(o, tok * 2, g, tok * 4) ||
-      overlap(o, tok * 2, beta, T * H * 4))
+      overlap(o, tok * 2, beta, T * H * 4) ||
+      (pro.b && overlap(o, tok * 2, pro.b, ((T - 1) * pro.b_stride + H) * 2)))
     return KDA_ERR_INVALID_ARGUMENT;
   DecodeArgs da;
   da.q = static_cast<const uint16_t *>(q);
@@ -260,7 +284,57 @@ kda_status kda_decode_fwd(const void *q, const void *k, const void *v, const flo
   da.N = N;
   da.H = H;
   da.scale = scale;
+  da.b = pro.b;
+  da.b_stride = pro.b_stride;
+  da.qk_eps = pro.qk_eps;
   return hip_status(launch_decode(da, stream));
+}
+
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                         int64_t T, int32_t N, int32_t H, float scale, void *o,
+                         float *final_state, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  return chunk_fwd_impl(q, k, v, g, beta, initial_state, cu_seqlens, T, N, H, scale, o,
+                        final_state, workspace, workspace_bytes, stream, Prologue());
+}
+
+kda_status kda_chunk_fwd_fused(const void *q, const void *k, const void *v, const float *g,
+                               const void *b, int64_t b_stride, float qk_eps,
+                               const float *initial_state, const int32_t *cu_seqlens, int64_t T,
+                               int32_t N, int32_t H, float scale, void *o, float *final_state,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T > 0 && !b) return KDA_ERR_INVALID_ARGUMENT;
+  if (qk_eps != qk_eps) return KDA_ERR_INVALID_ARGUMENT;  // NaN
+  Prologue pro;
+  pro.b = static_cast<const uint16_t *>(b);
+  pro.b_stride = b_stride;
+  pro.qk_eps = qk_eps >= 0.f ? qk_eps : -1.f;
+  return chunk_fwd_impl(q, k, v, g, nullptr, initial_state, cu_seqlens, T, N, H, scale, o,
+                        final_state, workspace, workspace_bytes, stream, pro);
+}
+
+kda_status kda_decode_fwd(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                          int64_t T, int32_t N, int32_t H, float scale, void *o,
+                          float *final_state, hipStream_t stream) {
+  return decode_fwd_impl(q, k, v, g, beta, initial_state, cu_seqlens, T, N, H, scale, o,
+                         final_state, stream, Prologue());
+}
+
+kda_status kda_decode_fwd_fused(const void *q, const void *k, const void *v, const float *g,
+                                const void *b, int64_t b_stride, float qk_eps,
+                                const float *initial_state, const int32_t *cu_seqlens, int64_t T,
+                                int32_t N, int32_t H, float scale, void *o, float *final_state,
+                                hipStream_t stream) {
+  if (T > 0 && !b) return KDA_ERR_INVALID_ARGUMENT;
+  if (qk_eps != qk_eps) return KDA_ERR_INVALID_ARGUMENT;  // NaN
+  Prologue pro;
+  pro.b = static_cast<const uint16_t *>(b);
+  pro.b_stride = b_stride;
+  pro.qk_eps = qk_eps >= 0.f ? qk_eps : -1.f;
+  return decode_fwd_impl(q, k, v, g, nullptr, initial_state, cu_seqlens, T, N, H, scale, o,
+                         final_state, stream, pro);
 }
 
 kda_status kda_chunk_recurrence(const float *initial_state, int64_t T, int32_t N, int32_t H,

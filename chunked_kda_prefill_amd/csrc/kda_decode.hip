@@ -39,6 +39,7 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(DecodeArgs a) {
   __shared__ float ks[DK], qs[DK], eg[DK];
   __shared__ float red[DEC_WAVES][DEC_COLS];
+  __shared__ float nrm[DEC_WAVES];
   const int64_t wg = blockIdx.x;
   const int half = (int)(wg % (DV / DEC_COLS));
   const int64_t sh = wg / (DV / DEC_COLS);
@@ -64,22 +65,40 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(DecodeArgs a) {
 
   for (int64_t t = t_beg; t < t_end; ++t) {
     const int64_t tok = (t * a.H + h) * DK;
+    float x;
     if (tid < DK) {
-      ks[tid] = bf16_to_f32(a.k[tok + tid]);
+      x = bf16_to_f32(a.k[tok + tid]);
+      ks[tid] = x;
       eg[tid] = expf(a.g[tok + tid]);
     } else {
-      qs[tid - DK] = bf16_to_f32(a.q[tok + tid - DK]);
+      x = bf16_to_f32(a.q[tok + tid - DK]);
+      qs[tid - DK] = x;
+    }
+    if (a.qk_eps >= 0.f) {
+      // fused prologue: the squared norms of k (waves 0, 1) and q (waves 2,
+      // 3), a butterfly within each wave, then two partial sums in LDS
+      float sq = x * x;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) sq += __shfl_xor(sq, m);
+      if (l == 0) nrm[w] = sq;
     }
     const float vv = bf16_to_f32(a.v[tok + col]);
-    const float beta = a.beta[t * a.H + h];
+    const float beta = a.b ? 1.f / (1.f + expf(-bf16_to_f32(a.b[t * a.b_stride + h])))
+                           : a.beta[t * a.H + h];
     __syncthreads();
+    float rk = 1.f, rq = 1.f;
+    if (a.qk_eps >= 0.f) {
+      const float sk = (nrm[0] + nrm[1]) + a.qk_eps, sq = (nrm[2] + nrm[3]) + a.qk_eps;
+      rk = sk > 0.f ? 1.f / sqrtf(sk) : 0.f;  // a zero row stays zero (qk_eps = 0)
+      rq = sq > 0.f ? 1.f / sqrtf(sq) : 0.f;
+    }
 
     // decay, then this wave's part of (S^T k)[col]
     float pu = 0.f;
 #pragma unroll
     for (int r = 0; r < DEC_ROWS; ++r) {
       S[r] *= eg[r0 + r];
-      pu = fmaf(S[r], ks[r0 + r], pu);
+      pu = fmaf(S[r], ks[r0 + r] * rk, pu);
     }
     red[w][l] = pu;
     __syncthreads();
@@ -90,8 +109,8 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(DecodeArgs a) {
     float po = 0.f;
 #pragma unroll
     for (int r = 0; r < DEC_ROWS; ++r) {
-      S[r] = fmaf(ks[r0 + r], d, S[r]);
-      po = fmaf(S[r], qs[r0 + r], po);
+      S[r] = fmaf(ks[r0 + r] * rk, d, S[r]);
+      po = fmaf(S[r], qs[r0 + r] * rq, po);
     }
     __syncthreads();  // every wave has read red (u) and ks, qs, eg
     red[w][l] = po;

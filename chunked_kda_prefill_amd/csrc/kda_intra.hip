@@ -237,9 +237,18 @@ __device__ __forceinline__ void load_unit(const IntraArgs &a, const int4 info, i
     for (int j = 0; j < 8; ++j)
       in.g[j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
                                                rg, 4 * (roff + slot_ch(j, grp)), 0, AUX_G));
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(a.beta + tb * a.H + h), 0, n * a.H * 4, BUF_DWORD3);
-    in.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * row * a.H, 0, AUX_G));
+    if (a.b) {
+      // beta logits (bf16) of a strided slice; the sigmoid is taken where
+      // beta is published (rows past n read 0 here and are set to 0 there)
+      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t *>(a.b + tb * a.b_stride + h), 0, (int)(n * a.b_stride * 2), BUF_DWORD3);
+      in.beta = bf16_bits_to_f32(
+          __builtin_amdgcn_raw_buffer_load_b16(rb, (int)(2 * row * a.b_stride), 0, AUX_G));
+    } else {
+      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float *>(a.beta + tb * a.H + h), 0, n * a.H * 4, BUF_DWORD3);
+      in.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * row * a.H, 0, AUX_G));
+    }
   }
   if (part < 0 || part == 1) {
     const __amdgpu_buffer_rsrc_t rq = unit_rsrc(a.q, tb, n, a.H, h, 2);
@@ -273,6 +282,7 @@ __device__ __forceinline__ void load_v(const IntraArgs &a, int64_t t0, int n, in
 
 // One (chunk, head) unit whose inputs are already in `nxt` (loads issued).
 // After the unit's own inputs are consumed, `nxt` receives the next unit's.
+template <bool NORM>
 __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, int c, int h,
                                            bool more, int cn, int hn, UnitInputs &nxt,
                                            const int32_t *first_lds, int &s_next) {
@@ -316,7 +326,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
     for (int j = 0; j < 8; ++j)
       *reinterpret_cast<float4 *>(&rt[(4 + w) * DK + slot_ch(j, grp)]) = G[j];
   }
-  if (grp == 0) sm.beta[row] = in.beta;
+  if (grp == 0) sm.beta[row] = a.b ? (row < n ? 1.f / (1.f + expf(-in.beta)) : 0.f) : in.beta;
   __syncthreads();
 
   // ---- per-channel tables (two threads per channel) ----
@@ -357,6 +367,32 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
     slab_to_slots(in.q[s], qs[2 * s], qs[2 * s + 1]);
     slab_to_slots(in.k[s], ks[2 * s], ks[2 * s + 1]);
   }
+  // fused prologue: the row's L2 norms (its 128 channels are spread over the
+  // lanes nn, nn + 16, nn + 32 and nn + 48; the two swap-and-add steps give
+  // all four the same sum)
+  float rq = 1.f, rk = 1.f;
+  if constexpr (NORM) {
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float f[4], e[4];
+      unpack4(qs[j], f);
+      unpack4(ks[j], e);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        sq = fmaf(f[x], f[x], sq);
+        sk = fmaf(e[x], e[x], sk);
+      }
+    }
+    sq += __shfl_xor(sq, 16);
+    sk += __shfl_xor(sk, 16);
+    sq += __shfl_xor(sq, 32);
+    sk += __shfl_xor(sk, 32);
+    // a zero row (the padding past a partial chunk's end, or zero input
+    // with qk_eps = 0) stays zero rather than 0 * inf
+    rq = sq + a.qk_eps > 0.f ? 1.f / sqrtf(sq + a.qk_eps) : 0.f;
+    rk = sk + a.qk_eps > 0.f ? 1.f / sqrtf(sk + a.qk_eps) : 0.f;
+  }
   uint2 kgb[8], kgm[8];
   bf16x8 qh[4], kh[4];
   f32x4 accA = zero4(), accL = zero4();
@@ -376,6 +412,13 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
       float qf[4], kf[4], kgv[4], kmv[4], ktv[4];
       unpack4(qs[j], qf);
       unpack4(ks[j], kf);
+      if constexpr (NORM) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qf[e] *= rq;
+          kf[e] *= rk;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float t = d[e] * LOG2E;
@@ -731,6 +774,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
 // stride of the grid size.  Each unit's inputs are loaded into registers
 // while the unit before it computes, and while one workgroup waits at a
 // barrier the other computes.
+template <bool NORM>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void intra_kernel(
     IntraArgs a) {
   __shared__ IntraSmem sm;
@@ -787,7 +831,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void in
       hn -= a.H;
       ++cn;
     }
-    intra_unit(a, sm, c, h, more, cn, hn, nxt, first_lds, s_next);
+    intra_unit<NORM>(a, sm, c, h, more, cn, hn, nxt, first_lds, s_next);
     if (!more) break;
     u += G;
     c = cn;
@@ -805,7 +849,10 @@ hipError_t launch_intra(const IntraArgs &a, hipStream_t stream) {
   const int64_t units = a.nc_max * a.H;
   const int64_t slots = 2 * (int64_t)cus;
   const int64_t grid = units < slots ? units : slots;
-  hipLaunchKernelGGL(intra_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, a);
+  if (a.qk_eps >= 0.f)
+    hipLaunchKernelGGL(intra_kernel<true>, dim3((unsigned)grid), dim3(NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL(intra_kernel<false>, dim3((unsigned)grid), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 

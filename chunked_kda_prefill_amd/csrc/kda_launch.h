@@ -30,6 +30,12 @@ struct IntraArgs {
   // workgroup 0 writes the workspace table; else chunk_table_kernel has
   // written it before this launch
   int32_t inline_table;
+  // fused prologue: beta = sigmoid(b[t * b_stride + h]) when b is set (bf16
+  // logits, beta unused); q and k L2-normalised per (token, head) as
+  // x / sqrt(sum x^2 + qk_eps) when qk_eps >= 0
+  const uint16_t *b;
+  int64_t b_stride;
+  float qk_eps;
 };
 hipError_t launch_intra(const IntraArgs &a, hipStream_t stream);
 
@@ -56,6 +62,9 @@ struct DecodeArgs {
   int64_t T;
   int32_t N, H;
   float scale;
+  const uint16_t *b;  // fused prologue, as in IntraArgs
+  int64_t b_stride;
+  float qk_eps;
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 

@@ -202,6 +202,21 @@ def decode_step(users: int, tokens: int, H: int) -> Workload:
                          seed=200 + 10 * tokens + users % 10, h0="normal")
 
 
+def raw_prologue_inputs(w: Workload, seed: int, pre: int = 5, post: int = 3):
+    """Inputs for the fused-prologue entry points, next to workload ``w``: q
+    and k drawn N(0,1) (not normalised; k scaled by 4 so that its rows are
+    far from unit norm) and beta logits N(0,1), all bf16, the logits as
+    columns [pre, pre + H) of a [T, pre + H + post] row-major tensor (the
+    strided slice of a projection output).  Returns (q, k, b_full, pre) as
+    bf16 bit patterns."""
+    rng = np.random.default_rng(seed)
+    T, H = w.T, w.H
+    q = f32_to_bf16_bits(_normal(rng, (T, H, DK)))
+    k = f32_to_bf16_bits(4.0 * _normal(rng, (T, H, DK)))
+    b = f32_to_bf16_bits(_normal(rng, (T, pre + H + post)))
+    return q, k, b, pre
+
+
 def small(lengths, H: int = 2, seed: int = 7, h0: str = "normal",
           pinned_fraction: float = 0.0, scale: Optional[float] = None) -> Workload:
     """A small ad-hoc workload for parity and edge-case tests."""

@@ -126,6 +126,39 @@ kda_status kda_decode_fwd(const void *q, const void *k, const void *v,
                           void *o, float *final_state, hipStream_t stream);
 
 /*
+ * The same two operations with the steps before them fused in ("Kimi K3
+ * Prefill PP16" notes, third throughput section, KDA switch table: beta is
+ * computed from a strided bf16 slice of the projection output, copy and
+ * sigmoid in one kernel; KDA TPU report, section 8: q and k are
+ * L2-normalised per token, as the model does):
+ *
+ *   b         bf16 beta logits; beta[t, h] = sigmoid(b[t * b_stride + h])
+ *             in fp32.  b points at the slice's first column (e.g. into a
+ *             [T, b_stride] row-major projection output); H <= b_stride <=
+ *             2^24; 2-byte aligned.  It replaces the fp32 beta argument.
+ *   qk_eps    >= 0: q and k are used as x / sqrt(sum_i x_i^2 + qk_eps) over
+ *             the 128 channels of each (token, head), computed in fp32 from
+ *             the bf16 inputs (an all-zero row stays zero); < 0: q and k are
+ *             used as given.  NaN is KDA_ERR_INVALID_ARGUMENT.
+ *
+ * All other arguments, and the results, are those of kda_chunk_fwd and
+ * kda_decode_fwd.  b must not overlap o.
+ */
+kda_status kda_chunk_fwd_fused(const void *q, const void *k, const void *v,
+                               const float *g, const void *b, int64_t b_stride,
+                               float qk_eps, const float *initial_state,
+                               const int32_t *cu_seqlens, int64_t T, int32_t N,
+                               int32_t H, float scale, void *o, float *final_state,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+kda_status kda_decode_fwd_fused(const void *q, const void *k, const void *v,
+                                const float *g, const void *b, int64_t b_stride,
+                                float qk_eps, const float *initial_state,
+                                const int32_t *cu_seqlens, int64_t T, int32_t N,
+                                int32_t H, float scale, void *o, float *final_state,
+                                hipStream_t stream);
+
+/*
  * Step-level entry points.  They run the steps of kda_chunk_fwd on their
  * own so that each step can be checked and timed separately; kda_chunk_fwd
  * does not call them.

@@ -123,6 +123,28 @@ def kda_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, scale=None,
     return o, fin
 
 
+def prologue(q, k, b, qk_eps=None):
+    """The steps fused in front of the recurrence, in fp64 ("Kimi K3 Prefill
+    PP16" notes, third throughput section, KDA switch table: beta from a bf16
+    slice of the projection output through a sigmoid; KDA TPU report,
+    section 8: q and k L2-normalised per token as the model does).  ``b`` holds the beta logits
+    [T, H] (bf16 bit patterns or float); beta = 1 / (1 + exp(-b)).  With
+    ``qk_eps`` given, each (token, head) row x of q and of k becomes
+    x / sqrt(sum x^2 + qk_eps).  Returns (q, k, beta), fp64."""
+    q, k, b = (widen(a).astype(np.float64) for a in (q, k, b))
+    beta = 1.0 / (1.0 + np.exp(-b))
+    if qk_eps is not None:
+        q, k = _unit_rows(q, qk_eps), _unit_rows(k, qk_eps)
+    return q, k, beta
+
+
+def _unit_rows(x, eps):
+    # x / sqrt(|x|^2 + eps); an all-zero row with eps = 0 (0/0) is read as
+    # zero, the limit of the eps > 0 case
+    d = np.sqrt((x * x).sum(axis=-1, keepdims=True) + eps)
+    return np.divide(x, d, out=np.zeros_like(x), where=d > 0)
+
+
 def _seq_ranges(cu):
     cu = np.asarray(cu, dtype=np.int64)
     return [(int(cu[s]), int(cu[s + 1])) for s in range(cu.shape[0] - 1)]

@@ -126,6 +126,29 @@ def test_decode_entry_rejects_bad_arguments():
     assert dec(h0=8 << 20, hT=(8 << 20) + 256) == INV     # partly overlapping states
 
 
+def test_fused_entries_reject_bad_arguments():
+    # host-checked argument errors of the fused entry points (no launch is reached)
+    lib = kda.load_library()
+    A = 1 << 20
+    def call(fn, **over):
+        a = dict(q=A, k=2 * A, v=3 * A, g=4 * A, b=5 * A, bs=2, eps=1e-6, h0=None, cu=6 * A,
+                 T=128, N=1, H=2, scale=1.0, o=7 * A, hT=8 * A)
+        a.update(over)
+        head = (a["q"], a["k"], a["v"], a["g"], a["b"], a["bs"], a["eps"], a["h0"], a["cu"],
+                a["T"], a["N"], a["H"], a["scale"], a["o"], a["hT"])
+        if fn == "chunk":
+            return lib.kda_chunk_fwd_fused(*head, 9 * A, 64 * A, None)
+        return lib.kda_decode_fwd_fused(*head, None)
+    INV = 1
+    for fn in ("chunk", "decode"):
+        assert call(fn, b=None) == INV                     # logits required when T > 0
+        assert call(fn, eps=float("nan")) == INV
+        assert call(fn, bs=1) == INV                       # row stride below H
+        assert call(fn, bs=1 << 25) == INV                 # row stride beyond 2^24
+        assert call(fn, b=(5 << 20) + 1) == INV            # misaligned logits
+        assert call(fn, o=(5 << 20) + 64) == INV           # o overlaps the logits
+
+
 def test_python_wrapper_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "_lib", None)
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))

@@ -242,3 +242,40 @@ def test_error_metrics():
     b = np.array([1.0, 2.0, 3.0])
     assert oracle.max_abs_err(a, b) == 1.0
     assert oracle.rel_fro_err(a, b) == pytest.approx(1.0 / math.sqrt(14.0))
+
+
+def test_prologue_sigmoid_closed_forms():
+    # sigmoid(0) = 1/2, sigmoid(+-ln 3) = 3/4 and 1/4, sigmoid(-x) = 1 - sigmoid(x)
+    x = np.array([[0.0, np.log(3.0), -np.log(3.0)]])
+    z = np.zeros((1, 3, 4))
+    _, _, beta = oracle.prologue(z, z, x)
+    assert np.allclose(beta, [[0.5, 0.75, 0.25]], rtol=0, atol=1e-15)
+    r = np.random.default_rng(21).normal(size=(5, 7))
+    _, _, b1 = oracle.prologue(np.zeros((5, 7, 2)), np.zeros((5, 7, 2)), r)
+    _, _, b2 = oracle.prologue(np.zeros((5, 7, 2)), np.zeros((5, 7, 2)), -r)
+    assert np.allclose(b1 + b2, 1.0, rtol=0, atol=1e-15)
+
+
+def test_prologue_l2norm_closed_forms():
+    rng = np.random.default_rng(22)
+    q = rng.normal(size=(6, 3, 128)) * 3.0
+    k = rng.normal(size=(6, 3, 128)) * 0.1
+    b = np.zeros((6, 3))
+    qn, kn, _ = oracle.prologue(q, k, b, qk_eps=0.0)
+    # unit rows, each a positive multiple of its input
+    assert np.allclose(np.linalg.norm(qn, axis=-1), 1.0, rtol=0, atol=1e-14)
+    assert np.allclose(np.linalg.norm(kn, axis=-1), 1.0, rtol=0, atol=1e-14)
+    cos = (qn * q).sum(-1) / np.linalg.norm(q, axis=-1)
+    assert np.allclose(cos, 1.0, rtol=0, atol=1e-14)
+    # with eps: |x'|^2 = s / (s + eps), s = |x|^2
+    eps = 1e-3
+    _, ke, _ = oracle.prologue(q, k, b, qk_eps=eps)
+    s2 = (k * k).sum(-1)
+    assert np.allclose((ke * ke).sum(-1), s2 / (s2 + eps), rtol=1e-13, atol=0)
+    # a zero row stays zero, also with eps = 0
+    z = np.zeros((2, 1, 128))
+    zq, _, _ = oracle.prologue(z, z, np.zeros((2, 1)), qk_eps=0.0)
+    assert np.array_equal(zq, z)
+    # without eps, q and k pass through
+    qp, kp, _ = oracle.prologue(q, k, b)
+    assert np.array_equal(qp, q) and np.array_equal(kp, k)
