@@ -195,6 +195,40 @@ def sweep(args, torch, np, kda, wl):
         del t, ws, o, fin
         if fused:
             del blog
+    norm_sweep(torch, np, kda, wl, dev, stream, flush, sink)
+
+
+def norm_sweep(torch, np, kda, wl, dev, stream, flush, sink):
+    """Cold latency of the gated-RMSNorm epilogue (kda_gated_rmsnorm) at the
+    output shapes of FUSED_SWEEP_CONFIGS: x = o [T, H, 128] contiguous, the
+    gate a column slice of a [T, H*128 + 128] bf16 tensor.  Algorithmic bytes
+    per (token, head) row: 256 read of x, 256 of the gate, 256 written."""
+    print("\n| epilogue config | T | H | median µs | p10 µs | p90 µs | GB/s | HBM frac |")
+    print("|---|---|---|---|---|---|---|---|")
+    for name in FUSED_SWEEP_CONFIGS:
+        w = wl.by_name(name)
+        T, H = w.T, w.H
+        x = torch.randn((T, H, 128), device=dev).to(torch.bfloat16)
+        zf = torch.randn((T, H * 128 + 128), device=dev).to(torch.bfloat16)
+        z = zf[:, 64:64 + H * 128].view(T, H, 128)
+        wt = torch.ones(128, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(20):
+            kda.gated_rmsnorm(x, z, wt, out=y)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(100)]
+        for a, b in evs:
+            torch.sum(flush, dim=0, out=sink)
+            a.record(stream)
+            kda.gated_rmsnorm(x, z, wt, out=y)
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        med, p10, p90 = (float(np.percentile(us, q)) for q in (50, 10, 90))
+        gbs = T * H * 768 / (med * 1e-6) / 1e9
+        print(f"| {w.name} (gated_rmsnorm) | {T} | {H} | {med:.1f} | {p10:.1f} | {p90:.1f} | "
+              f"{gbs:.0f} | {gbs / HBM_PEAK_GBS:.3f} |", flush=True)
+        del x, zf, z, y
 
 
 def main():

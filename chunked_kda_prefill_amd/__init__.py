@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     decode_fwd,
     decode_fwd_fused,
     gate_cumsum,
+    gated_rmsnorm,
     load_library,
     new_workspace,
     workspace_layout,

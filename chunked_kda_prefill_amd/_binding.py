@@ -26,7 +26,8 @@ STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPOR
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
             "kda_chunk_table", "kda_gate_cumsum", "kda_chunk_intra",
             "kda_workspace_layout", "kda_chunk_recurrence", "kda_decode_fwd",
-            "kda_chunk_fwd_fused", "kda_decode_fwd_fused")
+            "kda_chunk_fwd_fused", "kda_decode_fwd_fused", "kda_gated_rmsnorm")
+ACTIVATIONS = {"sigmoid": 0, "silu": 1}
 
 
 class KDAError(RuntimeError):
@@ -63,6 +64,8 @@ def load_library():
     lib.kda_chunk_fwd_fused.restype = ctypes.c_int
     lib.kda_decode_fwd_fused.argtypes = [P, P, P, P, P, I64, F32, P, P, I64, I32, I32, F32, P, P, P]
     lib.kda_decode_fwd_fused.restype = ctypes.c_int
+    lib.kda_gated_rmsnorm.argtypes = [P, I64, P, I64, P, F32, I32, I64, I32, P, P]
+    lib.kda_gated_rmsnorm.restype = ctypes.c_int
     lib.kda_chunk_table.argtypes = [P, I64, I32, P, P, P, P]
     lib.kda_chunk_table.restype = ctypes.c_int
     lib.kda_gate_cumsum.argtypes = [P, P, I64, I32, I32, P, P, SZ, P]
@@ -283,6 +286,44 @@ def decode_fwd_fused(q, k, v, g, b, cu_seqlens, initial_state=None, scale: Optio
         T, N, H, float(scale), _ptr(o), _ptr(final_state), _stream(q.device))
     _check("kda_decode_fwd_fused", st)
     return o, final_state
+
+
+def _rows(x, name: str):
+    """x: bf16 [T, H, 128] whose (head, channel) block is contiguous; returns
+    its token stride in elements."""
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if x.dtype != torch.bfloat16 or x.dim() != 3 or x.shape[2] != HEAD_DIM \
+            or x.stride(2) != 1 or x.stride(1) != HEAD_DIM:
+        raise ValueError(f"{name} must be a bf16 [T, H, 128] tensor with contiguous heads and "
+                         "channels (a token-strided view, e.g. a column slice, is fine)")
+    return int(x.stride(0)) if x.shape[0] > 1 else x.shape[1] * HEAD_DIM
+
+
+def gated_rmsnorm(x, gate, weight, eps: float = 1e-6, activation: str = "sigmoid", out=None):
+    """Gated RMSNorm after the operation (kda_gated_rmsnorm): per (token,
+    head) row, y = weight * x / sqrt(mean(x^2) + eps) * act(gate), act =
+    sigmoid or silu.  x, gate: bf16 [T, H, 128] (token-strided views are
+    fine); weight: fp32 [128].  Returns y, bf16 [T, H, 128]; out=x updates
+    x in place (x contiguous)."""
+    torch = _torch()
+    xs, zs = _rows(x, "x"), _rows(gate, "gate")
+    T, H = int(x.shape[0]), int(x.shape[1])
+    if tuple(gate.shape) != tuple(x.shape) or gate.device != x.device:
+        raise ValueError("gate must match x in shape and device")
+    _expect(weight, "weight", torch.float32, (HEAD_DIM,))
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}")
+    if out is None:
+        out = torch.empty((T, H, HEAD_DIM), dtype=torch.bfloat16, device=x.device)
+    else:
+        _expect(out, "out", torch.bfloat16, (T, H, HEAD_DIM))
+    st = load_library().kda_gated_rmsnorm(
+        _ptr(x), xs, _ptr(gate), zs, _ptr(weight), float(eps), ACTIVATIONS[activation], T, H,
+        _ptr(out), _stream(x.device))
+    _check("kda_gated_rmsnorm", st)
+    return out
 
 
 def chunk_table(cu_seqlens, T: int):

@@ -337,6 +337,46 @@ kda_status kda_decode_fwd_fused(const void *q, const void *k, const void *v, con
                          final_state, stream, pro);
 }
 
+kda_status kda_gated_rmsnorm(const void *x, int64_t x_stride, const void *gate,
+                             int64_t gate_stride, const float *weight, float eps,
+                             int32_t activation, int64_t T, int32_t H, void *y,
+                             hipStream_t stream) {
+  if (T < 0 || H < 1) return KDA_ERR_INVALID_ARGUMENT;
+  if (T > INT32_MAX || H > 65535) return KDA_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f) || eps == INFINITY) return KDA_ERR_INVALID_ARGUMENT;  // NaN, < 0, inf
+  if (activation != KDA_ACT_SIGMOID && activation != KDA_ACT_SILU)
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (T == 0) return KDA_OK;
+  const int64_t row = (int64_t)H * DK;
+  if (!x || !gate || !weight || !y) return KDA_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(gate, 16) || !aligned(weight, 16) || !aligned(y, 16))
+    return KDA_ERR_INVALID_ARGUMENT;
+  // 16-byte row segments: strides are whole multiples of 8 elements
+  if (x_stride < row || gate_stride < row || x_stride % 8 || gate_stride % 8 ||
+      x_stride > ((int64_t)1 << 40) || gate_stride > ((int64_t)1 << 40))
+    return KDA_ERR_INVALID_ARGUMENT;
+  const int64_t ybytes = T * row * 2;
+  const int64_t xbytes = ((T - 1) * x_stride + row) * 2;
+  const int64_t zbytes = ((T - 1) * gate_stride + row) * 2;
+  // y may be x itself (in place, contiguous x), and nothing else it reads
+  const bool in_place = y == x && x_stride == row;
+  if ((!in_place && overlap(y, ybytes, x, xbytes)) || overlap(y, ybytes, gate, zbytes) ||
+      overlap(y, ybytes, weight, DK * 4))
+    return KDA_ERR_INVALID_ARGUMENT;
+  NormArgs na;
+  na.x = static_cast<const uint16_t *>(x);
+  na.z = static_cast<const uint16_t *>(gate);
+  na.w = weight;
+  na.y = static_cast<uint16_t *>(y);
+  na.x_stride = x_stride;
+  na.z_stride = gate_stride;
+  na.T = T;
+  na.H = H;
+  na.eps = eps;
+  na.act = activation;
+  return hip_status(launch_gated_rmsnorm(na, stream));
+}
+
 kda_status kda_chunk_recurrence(const float *initial_state, int64_t T, int32_t N, int32_t H,
                                 void *o, float *final_state, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream) {

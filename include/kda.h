@@ -159,6 +159,38 @@ kda_status kda_decode_fwd_fused(const void *q, const void *k, const void *v,
                                 hipStream_t stream);
 
 /*
+ * The gated RMSNorm that follows the operation in the model ("Kimi K3
+ * Prefill PP16" notes, third throughput section, KDA switch table: the KDA
+ * output tail reads its strided input directly; RMSNorm after Zhang and
+ * Sennrich, cited by the KDA TPU report).  Per (token t, head h) row of 128
+ * channels:
+ *
+ *   y[t, h, :] = weight * x / sqrt(mean(x^2) + eps) * act(gate)
+ *
+ * with act(z) = 1 / (1 + exp(-z)) (KDA_ACT_SIGMOID) or z / (1 + exp(-z))
+ * (KDA_ACT_SILU), in fp32, y rounded to bf16 (nearest even).  An all-zero
+ * row with eps = 0 stays zero.
+ *
+ *   x, gate   bf16; row (t, h) at element t * stride + h * 128, with
+ *             x_stride, gate_stride >= H * 128 and multiples of 8 (16-byte
+ *             row segments), e.g. column slices of a row-major [T, stride]
+ *             tensor.  16-byte aligned.
+ *   weight    fp32 [128], 16-byte aligned.
+ *   eps       >= 0 and finite.
+ *   y         bf16 [T, H, 128] contiguous, 16-byte aligned.  y == x (with
+ *             x_stride = H * 128) updates in place; otherwise y must not
+ *             overlap x, gate or weight.
+ *
+ * T = 0 is a no-op.  Invalid arguments return KDA_ERR_INVALID_ARGUMENT
+ * before any launch; T > 2^31 - 1 or H > 65535 return KDA_ERR_UNSUPPORTED.
+ */
+enum { KDA_ACT_SIGMOID = 0, KDA_ACT_SILU = 1 };
+kda_status kda_gated_rmsnorm(const void *x, int64_t x_stride, const void *gate,
+                             int64_t gate_stride, const float *weight, float eps,
+                             int32_t activation, int64_t T, int32_t H, void *y,
+                             hipStream_t stream);
+
+/*
  * Step-level entry points.  They run the steps of kda_chunk_fwd on their
  * own so that each step can be checked and timed separately; kda_chunk_fwd
  * does not call them.

@@ -145,6 +145,24 @@ def _unit_rows(x, eps):
     return np.divide(x, d, out=np.zeros_like(x), where=d > 0)
 
 
+def gated_rmsnorm(x, gate, weight, eps, act="sigmoid"):
+    """The gated RMSNorm that follows the operation, in fp64 ("Kimi K3
+    Prefill PP16" notes, third throughput section, KDA switch table: the
+    KDA output tail; RMSNorm as defined by Zhang and Sennrich, whom the KDA
+    TPU report cites).  Per (token, head) row x of 128 channels, with gate
+    row z and weight w [128]:  y = w * x / sqrt(mean(x^2) + eps) * act(z),
+    act(z) = 1 / (1 + exp(-z)) ("sigmoid") or z / (1 + exp(-z)) ("silu").
+    An all-zero row with eps = 0 (0/0) is read as zero.  ``x`` and ``gate``
+    are [T, H, 128] (bf16 bit patterns or float); returns y, fp64."""
+    x, z = widen(x).astype(np.float64), widen(gate).astype(np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    sig = 1.0 / (1.0 + np.exp(-z))
+    a = {"sigmoid": sig, "silu": z * sig}[act]
+    d = np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    xn = np.divide(x, d, out=np.zeros_like(x), where=d > 0)
+    return w * xn * a
+
+
 def _seq_ranges(cu):
     cu = np.asarray(cu, dtype=np.int64)
     return [(int(cu[s]), int(cu[s + 1])) for s in range(cu.shape[0] - 1)]

@@ -149,6 +149,31 @@ def test_fused_entries_reject_bad_arguments():
         assert call(fn, o=(5 << 20) + 64) == INV           # o overlaps the logits
 
 
+def test_gated_rmsnorm_rejects_bad_arguments():
+    # host-checked argument errors of kda_gated_rmsnorm (no launch is reached)
+    lib = kda.load_library()
+    A = 1 << 20
+    def call(**over):
+        a = dict(x=A, xs=256, z=2 * A, zs=256, w=3 * A, eps=1e-6, act=0, T=16, H=2, y=4 * A)
+        a.update(over)
+        return lib.kda_gated_rmsnorm(a["x"], a["xs"], a["z"], a["zs"], a["w"], a["eps"],
+                                     a["act"], a["T"], a["H"], a["y"], None)
+    INV, UNS = 1, 2
+    assert call(T=0, x=None, y=None) == 0                 # empty: no-op
+    assert call(x=None) == INV
+    assert call(w=None) == INV
+    assert call(act=2) == INV
+    assert call(eps=-1.0) == INV
+    assert call(eps=float("nan")) == INV
+    assert call(eps=float("inf")) == INV
+    assert call(xs=255) == INV                            # below H * 128
+    assert call(zs=260) == INV                            # not a multiple of 8
+    assert call(z=2 * A + 8) == INV                       # misaligned
+    assert call(y=A + 512) == INV                         # y overlaps x (not in place)
+    assert call(y=2 * A) == INV                           # y is the gate
+    assert call(H=70000, xs=70000 * 128, zs=70000 * 128) == UNS
+
+
 def test_python_wrapper_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "_lib", None)
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))

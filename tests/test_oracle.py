@@ -279,3 +279,40 @@ def test_prologue_l2norm_closed_forms():
     # without eps, q and k pass through
     qp, kp, _ = oracle.prologue(q, k, b)
     assert np.array_equal(qp, q) and np.array_equal(kp, k)
+
+
+def test_gated_rmsnorm_closed_forms():
+    rng = np.random.default_rng(23)
+    x = rng.normal(size=(5, 3, 128)) * rng.uniform(0.1, 10, size=(5, 3, 1))
+    w1, big = np.ones(128), np.full((5, 3, 128), 40.0)   # sigmoid(40) = 1 in fp64
+    # eps = 0, unit weight, open gate: every row has mean square 1
+    y = oracle.gated_rmsnorm(x, big, w1, 0.0)
+    assert np.allclose((y * y).mean(-1), 1.0, rtol=0, atol=1e-13)
+    # scale invariance and oddness at eps = 0
+    assert np.allclose(oracle.gated_rmsnorm(3.5 * x, big, w1, 0.0), y, rtol=0, atol=1e-13)
+    assert np.allclose(oracle.gated_rmsnorm(-x, big, w1, 0.0), -y, rtol=0, atol=1e-13)
+    # with eps: mean(y^2) = ms / (ms + eps)
+    ms = (x * x).mean(-1)
+    ye = oracle.gated_rmsnorm(x, big, w1, 0.5)
+    assert np.allclose((ye * ye).mean(-1), ms / (ms + 0.5), rtol=1e-13, atol=0)
+    # a constant row c: y = w * c / sqrt(c^2 + eps) * act(z)
+    c = np.full((1, 1, 128), -2.0)
+    w = rng.uniform(-1, 1, size=128)
+    z = np.zeros((1, 1, 128))
+    yc = oracle.gated_rmsnorm(c, z, w, 1.0)
+    assert np.allclose(yc[0, 0], w * (-2.0 / np.sqrt(5.0)) * 0.5, rtol=1e-14, atol=0)
+    # SiLU: silu(0) = 0, silu(ln 3) = 0.75 ln 3, silu(-ln 3) = -0.25 ln 3
+    assert np.array_equal(oracle.gated_rmsnorm(c, z, w, 1.0, act="silu"), np.zeros_like(c))
+    zl = np.full((1, 1, 128), np.log(3.0))
+    ys = oracle.gated_rmsnorm(c, zl, w1, 0.0, act="silu")
+    assert np.allclose(ys, -0.75 * np.log(3.0), rtol=1e-14, atol=0)
+    ys = oracle.gated_rmsnorm(c, -zl, w1, 0.0, act="silu")
+    assert np.allclose(ys, 0.25 * np.log(3.0), rtol=1e-14, atol=0)
+    # weights act per channel; a zero row stays zero with eps = 0
+    e = np.zeros(128)
+    e[5] = 2.0
+    ye = oracle.gated_rmsnorm(x, big, e, 0.0)
+    assert np.count_nonzero(ye[..., np.arange(128) != 5]) == 0
+    assert np.allclose(ye[..., 5], 2.0 * y[..., 5], rtol=1e-14, atol=0)
+    zr = oracle.gated_rmsnorm(np.zeros((2, 1, 128)), big[:2, :1], w1, 0.0)
+    assert np.array_equal(zr, np.zeros((2, 1, 128)))
