@@ -34,6 +34,30 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
+// Sum over the 64 lanes of a wave, in VALU cross-lane steps only: DPP
+// within each 16-lane row (xor 1, xor 2 by quad permutes, then the half-row
+// and row mirrors), then the permlane swaps between rows 0-1 / 2-3 and
+// between the two halves.  With both operands x, v_permlane16_swap returns
+// the even rows' partners in .second and the odd rows' in .first, and
+// v_permlane32_swap the low half's in .second and the high half's in .first.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float wave_sum(float x, int lane) {
+  x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = dpp_add<0x141>(x);  // row_half_mirror
+  x = dpp_add<0x140>(x);  // row_mirror
+  const uint32_t u = __float_as_uint(x);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x += __uint_as_float(((lane >> 4) & 1) ? p16[0] : p16[1]);
+  const uint32_t v = __float_as_uint(x);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  x += __uint_as_float(lane >= 32 ? p32[0] : p32[1]);
+  return x;
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(DecodeArgs a) {
@@ -63,28 +87,51 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(DecodeArgs a) {
   for (int r = 0; r < DEC_ROWS; ++r)
     S[r] = a.h0 ? a.h0[st_base + (int64_t)(r0 + r) * DV + col] : 0.f;
 
+  // a token's inputs, per thread: its k (threads 0-127, with g) or q
+  // element, its value column and beta (or the beta logit)
+  struct Tok {
+    uint16_t x, v;  // raw bits: nothing waits on a load before its use
+    uint32_t b;     // the beta logit's bf16 bits, or fp32 beta's bits
+    float g;
+  };
+  auto load_tok = [&](int64_t t) {
+    const int64_t tok = (t * a.H + h) * DK;
+    Tok r;
+    if (tid < DK) {
+      r.x = a.k[tok + tid];
+      r.g = a.g[tok + tid];
+    } else {
+      r.x = a.q[tok + tid - DK];
+      r.g = 0.f;
+    }
+    r.v = a.v[tok + col];
+    r.b = a.b ? (uint32_t)a.b[t * a.b_stride + h] : __float_as_uint(a.beta[t * a.H + h]);
+    return r;
+  };
+  Tok cur = {0, 0, 0u, 0.f};
+  if (t_beg < t_end) cur = load_tok(t_beg);
+
   for (int64_t t = t_beg; t < t_end; ++t) {
     const int64_t tok = (t * a.H + h) * DK;
-    float x;
+    // the next token's loads are in flight while this token is applied
+    Tok nxt = cur;
+    if (t + 1 < t_end) nxt = load_tok(t + 1);
+    const float x = bf16_to_f32(cur.x);
     if (tid < DK) {
-      x = bf16_to_f32(a.k[tok + tid]);
       ks[tid] = x;
-      eg[tid] = expf(a.g[tok + tid]);
+      eg[tid] = expf(cur.g);
     } else {
-      x = bf16_to_f32(a.q[tok + tid - DK]);
       qs[tid - DK] = x;
     }
     if (a.qk_eps >= 0.f) {
       // fused prologue: the squared norms of k (waves 0, 1) and q (waves 2,
-      // 3), a butterfly within each wave, then two partial sums in LDS
-      float sq = x * x;
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) sq += __shfl_xor(sq, m);
+      // 3), a cross-lane sum within each wave, then two partial sums in LDS
+      const float sq = wave_sum(x * x, l);
       if (l == 0) nrm[w] = sq;
     }
-    const float vv = bf16_to_f32(a.v[tok + col]);
-    const float beta = a.b ? 1.f / (1.f + expf(-bf16_to_f32(a.b[t * a.b_stride + h])))
-                           : a.beta[t * a.H + h];
+    const float vv = bf16_to_f32(cur.v);
+    const float beta = a.b ? 1.f / (1.f + expf(-bf16_to_f32((uint16_t)cur.b)))
+                           : __uint_as_float(cur.b);
     __syncthreads();
     float rk = 1.f, rq = 1.f;
     if (a.qk_eps >= 0.f) {
@@ -121,6 +168,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(DecodeArgs a) {
     }
     // the next token's staging writes come after wave 0 has read red: it
     // reaches the next barrier only after that read
+    cur = nxt;
   }
 
   if (a.hT) {
