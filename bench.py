@@ -61,7 +61,8 @@ def parse():
 
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, if it was taken on this workload with these kernel sources."""
+    summary, if it was taken on this workload with this kernel's current
+    sources (its translation unit, the headers it includes, the flags)."""
     import re
     from chunked_kda_prefill_amd import build as kbuild
     path = os.path.join(ROOT, "profiles", "headline_hbm_traffic.md")
@@ -73,10 +74,11 @@ def measured_traffic(workload: str, kernel: str):
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("source_hash") != kbuild.source_hash() or rec.get("workload") != workload:
+    unit = kbuild.KERNEL_UNITS.get(kernel)
+    if unit is None or rec.get("workload") != workload:
         return None
     k = rec.get(kernel)
-    if k is None:
+    if k is None or k.get("kernel_hash") != kbuild.kernel_hash(unit):
         return None
     return int(round((k["fetch_kib"] * rec["fetch_factor"] + k["write_kib"] * rec["write_factor"]) * 1024))
 

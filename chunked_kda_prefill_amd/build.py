@@ -50,6 +50,37 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def kernel_files(unit: str):
+    """The translation unit csrc/<unit> and every csrc header it includes,
+    directly or not."""
+    import re
+    todo, seen = [unit], []
+    while todo:
+        f = todo.pop()
+        if f in seen or not os.path.exists(os.path.join(CSRC, f)):
+            continue
+        seen.append(f)
+        with open(os.path.join(CSRC, f)) as fh:
+            todo += re.findall(r'^#include "([^"]+)"', fh.read(), re.M)
+    return sorted(seen)
+
+
+def kernel_hash(unit: str) -> str:
+    """Short sha256 over one kernel's sources (kernel_files) and the compile
+    flags: counter readings of that kernel stay valid while it is unchanged,
+    whatever else in the library changes."""
+    h = hashlib.sha256(" ".join(HIPCC_FLAGS).encode())
+    for f in kernel_files(unit):
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# the kernels whose counters the bench reports, by translation unit
+KERNEL_UNITS = {"kda_intra": "kda_intra.hip", "kda_recurrence": "kda_recurrence.hip"}
+
+
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "hipcc")
     tmp = LIB + f".tmp{os.getpid()}"
