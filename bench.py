@@ -87,7 +87,7 @@ SWEEP_CONFIGS = ["tiny", "headline"] + [f"batch{b}" for b in (1, 2, 4, 8, 16, 32
     ["sharegpt", "long", "decode16x1_h12", "decode16x4_h12", "decode64x1_h16", "decode64x1_h96"]
 # configs also timed through the fused-prologue entry points, and with the
 # same prologue done by separate torch ops in front of the plain entry point
-FUSED_SWEEP_CONFIGS = ("headline", "long", "decode16x4_h12", "decode64x1_h96")
+FUSED_SWEEP_CONFIGS = ("headline", "long", "decode16x1_h12", "decode16x4_h12", "decode64x1_h96")
 
 
 def sweep(args, torch, np, kda, wl):
@@ -101,7 +101,9 @@ def sweep(args, torch, np, kda, wl):
     bounded sample (a few heads) of the same inputs.  Decode configs are
     also timed through kda_decode_fwd; the FUSED_SWEEP_CONFIGS also through
     the fused-prologue entry points (raw q, k and strided bf16 beta logits),
-    and with that prologue done by torch ops before the plain entry point."""
+    and with that prologue done by torch ops before the plain entry point;
+    their decode configs also as a whole decode step with the gated RMSNorm
+    (kda_decode_step_fused, and kda_decode_fwd_fused + kda_gated_rmsnorm)."""
     import oracle
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
@@ -131,6 +133,8 @@ def sweep(args, torch, np, kda, wl):
         main = ["decode_fwd", "chunk_fwd"] if n.startswith("decode") else ["chunk_fwd"]
         if n in FUSED_SWEEP_CONFIGS:
             main = main + [e + "_fused" for e in main] + ["torch prologue + " + main[0]]
+            if n.startswith("decode"):
+                main += ["decode_step_fused", "norm after decode_fwd_fused"]
         runs += [(n, e) for e in main]
     for name, entry in runs:
         w = wl.by_name(name)
@@ -140,16 +144,32 @@ def sweep(args, torch, np, kda, wl):
         o = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
         fin = torch.empty((N, H, 128, 128), dtype=torch.float32, device=dev)
         fused = "fused" in entry or "prologue" in entry
+        step = entry in ("decode_step_fused", "norm after decode_fwd_fused")
         if fused:
             # raw q, k and bf16 beta logits in a strided [T, 5 + H + 3] slice
             rq, rk, bfull, pre = wl.raw_prologue_inputs(w, 300)
             bf = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(
                 dev).view(torch.bfloat16)
             t["q"], t["k"], blog = bf(rq), bf(rk), bf(bfull)[:, pre:pre + H]
+        if step:
+            zfull = torch.randn((T, H * 128 + 128), device=dev).to(torch.bfloat16)
+            z = zfull[:, 64:64 + H * 128].view(T, H, 128)
+            nwt = torch.ones(128, dtype=torch.float32, device=dev)
+            ybuf = torch.empty_like(o)
         is_dec = entry.split(" + ")[-1].startswith("decode_fwd")
         plain = kda.decode_fwd if is_dec else kda.chunk_fwd
         extra = {} if is_dec else {"workspace": ws}
-        if entry.endswith("_fused"):
+        if entry == "decode_step_fused":
+            call = lambda: kda.decode_step_fused(
+                t["q"], t["k"], t["v"], t["g"], blog, t["cu_seqlens"], z, nwt,
+                initial_state=t["initial_state"], scale=w.scale, o=o, y=ybuf, final_state=fin)
+        elif entry == "norm after decode_fwd_fused":
+            def call():
+                kda.decode_fwd_fused(t["q"], t["k"], t["v"], t["g"], blog, t["cu_seqlens"],
+                                     initial_state=t["initial_state"], scale=w.scale, o=o,
+                                     final_state=fin)
+                kda.gated_rmsnorm(o, z, nwt, out=ybuf)
+        elif entry.endswith("_fused"):
             fn = kda.decode_fwd_fused if entry == "decode_fwd_fused" else kda.chunk_fwd_fused
             call = lambda: fn(t["q"], t["k"], t["v"], t["g"], blog, t["cu_seqlens"],
                               initial_state=t["initial_state"], scale=w.scale, qk_eps=1e-6,
@@ -190,6 +210,8 @@ def sweep(args, torch, np, kda, wl):
         cw = time.perf_counter() - c0
         otps = T * len(hs) / H / cw
         label = w.name if entry == "chunk_fwd" else f"{w.name} ({entry.replace('_fwd', '')})"
+        if step:
+            del zfull, z, ybuf
         print(f"| {label} | {T} | {N} | {H} | {w.num_chunks()} | {med:.1f} | {p10:.1f} | "
               f"{p90:.1f} | {T / med:.2f} | {gbs:.0f} | {gbs / HBM_PEAK_GBS:.3f} | "
               f"{flops / (med * 1e-6) / 1e12:.1f} | {otps:,.0f} ({len(hs)}) | "

@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     chunk_table,
     decode_fwd,
     decode_fwd_fused,
+    decode_step_fused,
     gate_cumsum,
     gated_rmsnorm,
     load_library,

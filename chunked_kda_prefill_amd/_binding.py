@@ -26,7 +26,8 @@ STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARGUMENT", 2: "KDA_ERR_UNSUPPOR
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
             "kda_chunk_table", "kda_gate_cumsum", "kda_chunk_intra",
             "kda_workspace_layout", "kda_chunk_recurrence", "kda_decode_fwd",
-            "kda_chunk_fwd_fused", "kda_decode_fwd_fused", "kda_gated_rmsnorm")
+            "kda_chunk_fwd_fused", "kda_decode_fwd_fused", "kda_gated_rmsnorm",
+            "kda_decode_step_fused")
 ACTIVATIONS = {"sigmoid": 0, "silu": 1}
 
 
@@ -66,6 +67,9 @@ def load_library():
     lib.kda_decode_fwd_fused.restype = ctypes.c_int
     lib.kda_gated_rmsnorm.argtypes = [P, I64, P, I64, P, F32, I32, I64, I32, P, P]
     lib.kda_gated_rmsnorm.restype = ctypes.c_int
+    lib.kda_decode_step_fused.argtypes = [P, P, P, P, P, I64, F32, P, P, I64, I32, I32, F32,
+                                          P, I64, P, F32, I32, P, P, P, P]
+    lib.kda_decode_step_fused.restype = ctypes.c_int
     lib.kda_chunk_table.argtypes = [P, I64, I32, P, P, P, P]
     lib.kda_chunk_table.restype = ctypes.c_int
     lib.kda_gate_cumsum.argtypes = [P, P, I64, I32, I32, P, P, SZ, P]
@@ -324,6 +328,40 @@ def gated_rmsnorm(x, gate, weight, eps: float = 1e-6, activation: str = "sigmoid
         _ptr(out), _stream(x.device))
     _check("kda_gated_rmsnorm", st)
     return out
+
+
+def decode_step_fused(q, k, v, g, b, cu_seqlens, gate, norm_weight, initial_state=None,
+                      scale: Optional[float] = None, qk_eps: Optional[float] = 1e-6,
+                      norm_eps: float = 1e-6, activation: str = "sigmoid",
+                      output_final_state: bool = True, o=None, y=None, final_state=None):
+    """A whole decode step in one kernel (kda_decode_step_fused):
+    decode_fwd_fused, then gated_rmsnorm(o, gate, norm_weight) on o's fp32
+    rows.  gate: bf16 [T, H, 128] (token-strided views are fine).  Returns
+    (o, y, final_state)."""
+    torch = _torch()
+    T, N, H = _check_inputs(q, k, v, g, None, cu_seqlens)
+    stride = _beta_logits(b, T, H)
+    zs = _rows(gate, "gate")
+    if tuple(gate.shape) != (T, H, HEAD_DIM):
+        raise ValueError(f"gate must have shape {(T, H, HEAD_DIM)}")
+    _expect(norm_weight, "norm_weight", torch.float32, (HEAD_DIM,))
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}")
+    o, final_state = _fused_outputs(q, cu_seqlens, initial_state, o, final_state,
+                                    output_final_state, T, N, H)
+    if y is None:
+        y = torch.empty((T, H, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
+    else:
+        _expect(y, "y", torch.bfloat16, (T, H, HEAD_DIM))
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    st = load_library().kda_decode_step_fused(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(b), stride,
+        -1.0 if qk_eps is None else float(qk_eps), _ptr(initial_state), _ptr(cu_seqlens),
+        T, N, H, float(scale), _ptr(gate), zs, _ptr(norm_weight), float(norm_eps),
+        ACTIVATIONS[activation], _ptr(o), _ptr(y), _ptr(final_state), _stream(q.device))
+    _check("kda_decode_step_fused", st)
+    return o, y, final_state
 
 
 def chunk_table(cu_seqlens, T: int):

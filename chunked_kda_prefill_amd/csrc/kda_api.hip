@@ -253,11 +253,21 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
   return run_recurrence(initial_state, T, N, H, o, final_state, ws, stream);
 }
 
+// The gated-RMSNorm epilogue fused into the decode kernel (y set).
+struct Epilogue {
+  void *y = nullptr;
+  const void *z = nullptr;
+  int64_t z_stride = 0;
+  const float *nw = nullptr;
+  float eps = 0.f;
+  int32_t act = KDA_ACT_SIGMOID;
+};
+
 static kda_status decode_fwd_impl(const void *q, const void *k, const void *v, const float *g,
                                   const float *beta, const float *initial_state,
                                   const int32_t *cu_seqlens, int64_t T, int32_t N, int32_t H,
                                   float scale, void *o, float *final_state, hipStream_t stream,
-                                  const Prologue &pro) {
+                                  const Prologue &pro, const Epilogue &epi = Epilogue()) {
   kda_status st = check_sizes(T, N, H);
   if (st != KDA_OK) return st;
   if ((int64_t)N * H * 2 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
@@ -270,6 +280,26 @@ static kda_status decode_fwd_impl(const void *q, const void *k, const void *v, c
       overlap(o, tok * 2, beta, T * H * 4) ||
       (pro.b && overlap(o, tok * 2, pro.b, ((T - 1) * pro.b_stride + H) * 2)))
     return KDA_ERR_INVALID_ARGUMENT;
+  if (epi.y && T > 0) {
+    if (!epi.z || !epi.nw || !aligned(epi.y, 2) || !aligned(epi.z, 2) || !aligned(epi.nw, 4))
+      return KDA_ERR_INVALID_ARGUMENT;
+    if (!(epi.eps >= 0.f) || epi.eps == INFINITY) return KDA_ERR_INVALID_ARGUMENT;
+    if (epi.act != KDA_ACT_SIGMOID && epi.act != KDA_ACT_SILU) return KDA_ERR_INVALID_ARGUMENT;
+    const int64_t row = (int64_t)H * DK;
+    if (epi.z_stride < row || epi.z_stride > ((int64_t)1 << 40)) return KDA_ERR_INVALID_ARGUMENT;
+    const int64_t zbytes = ((T - 1) * epi.z_stride + row) * 2;
+    const int64_t st_bytes = (int64_t)N * H * DK * DV * 4;
+    // y is written: it overlaps nothing else the call reads or writes
+    const void *others[] = {q, k, v, g, o, epi.z};
+    const int64_t sizes[] = {tok * 2, tok * 2, tok * 2, tok * 4, tok * 2, zbytes};
+    for (int i = 0; i < 6; ++i)
+      if (overlap(epi.y, tok * 2, others[i], sizes[i])) return KDA_ERR_INVALID_ARGUMENT;
+    if (overlap(epi.y, tok * 2, beta, T * H * 4) || overlap(epi.y, tok * 2, epi.nw, DV * 4) ||
+        overlap(epi.y, tok * 2, initial_state, st_bytes) ||
+        overlap(epi.y, tok * 2, final_state, st_bytes) ||
+        (pro.b && overlap(epi.y, tok * 2, pro.b, ((T - 1) * pro.b_stride + H) * 2)))
+      return KDA_ERR_INVALID_ARGUMENT;
+  }
   DecodeArgs da;
   da.q = static_cast<const uint16_t *>(q);
   da.k = static_cast<const uint16_t *>(k);
@@ -287,6 +317,12 @@ static kda_status decode_fwd_impl(const void *q, const void *k, const void *v, c
   da.b = pro.b;
   da.b_stride = pro.b_stride;
   da.qk_eps = pro.qk_eps;
+  da.y = static_cast<uint16_t *>(epi.y);
+  da.z = static_cast<const uint16_t *>(epi.z);
+  da.z_stride = epi.z_stride;
+  da.nw = epi.nw;
+  da.neps = epi.eps;
+  da.act = epi.act;
   return hip_status(launch_decode(da, stream));
 }
 
@@ -335,6 +371,30 @@ kda_status kda_decode_fwd_fused(const void *q, const void *k, const void *v, con
   pro.qk_eps = qk_eps >= 0.f ? qk_eps : -1.f;
   return decode_fwd_impl(q, k, v, g, nullptr, initial_state, cu_seqlens, T, N, H, scale, o,
                          final_state, stream, pro);
+}
+
+kda_status kda_decode_step_fused(const void *q, const void *k, const void *v, const float *g,
+                                 const void *b, int64_t b_stride, float qk_eps,
+                                 const float *initial_state, const int32_t *cu_seqlens, int64_t T,
+                                 int32_t N, int32_t H, float scale, const void *gate,
+                                 int64_t gate_stride, const float *norm_weight, float norm_eps,
+                                 int32_t activation, void *o, void *y, float *final_state,
+                                 hipStream_t stream) {
+  if (T > 0 && (!b || !y)) return KDA_ERR_INVALID_ARGUMENT;
+  if (qk_eps != qk_eps) return KDA_ERR_INVALID_ARGUMENT;  // NaN
+  Prologue pro;
+  pro.b = static_cast<const uint16_t *>(b);
+  pro.b_stride = b_stride;
+  pro.qk_eps = qk_eps >= 0.f ? qk_eps : -1.f;
+  Epilogue epi;
+  epi.y = T > 0 ? y : nullptr;
+  epi.z = gate;
+  epi.z_stride = gate_stride;
+  epi.nw = norm_weight;
+  epi.eps = norm_eps;
+  epi.act = activation;
+  return decode_fwd_impl(q, k, v, g, nullptr, initial_state, cu_seqlens, T, N, H, scale, o,
+                         final_state, stream, pro, epi);
 }
 
 kda_status kda_gated_rmsnorm(const void *x, int64_t x_stride, const void *gate,

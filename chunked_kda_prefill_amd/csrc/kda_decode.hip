@@ -60,19 +60,28 @@ __device__ __forceinline__ float wave_sum(float x, int lane) {
 
 }  // namespace
 
+// COLS value columns per workgroup: 64 (two workgroups per (sequence,
+// head), lane l holding column l of its half), or 128 with the gated-RMSNorm
+// epilogue fused in (one workgroup per (sequence, head), lane l holding
+// columns l and l + 64, so wave 0 ends up with the whole output row).
+template <int COLS>
 __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(DecodeArgs a) {
+  constexpr int NC = COLS / 64;  // columns per lane
+  constexpr bool EPI = COLS == DV;
   __shared__ float ks[DK], qs[DK], eg[DK];
-  __shared__ float red[DEC_WAVES][DEC_COLS];
+  __shared__ float red[DEC_WAVES][COLS];
   __shared__ float nrm[DEC_WAVES];
   const int64_t wg = blockIdx.x;
-  const int half = (int)(wg % (DV / DEC_COLS));
-  const int64_t sh = wg / (DV / DEC_COLS);
+  const int part = (int)(wg % (DV / COLS));
+  const int64_t sh = wg / (DV / COLS);
   const int h = (int)(sh % a.H);
   const int s = (int)(sh / a.H);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
-  const int col = half * DEC_COLS + l;
+  int col[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) col[j] = part * COLS + j * 64 + l;
   const int r0 = w * DEC_ROWS;
   const int64_t st_base = ((int64_t)s * a.H + h) * DK * DV;
 
@@ -82,16 +91,21 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(DecodeArgs a) {
   t_beg = t_beg < 0 ? 0 : (t_beg > a.T ? a.T : t_beg);
   t_end = t_end < t_beg ? t_beg : (t_end > a.T ? a.T : t_end);
 
-  float S[DEC_ROWS];
+  float S[NC][DEC_ROWS];
 #pragma unroll
-  for (int r = 0; r < DEC_ROWS; ++r)
-    S[r] = a.h0 ? a.h0[st_base + (int64_t)(r0 + r) * DV + col] : 0.f;
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int r = 0; r < DEC_ROWS; ++r)
+      S[j][r] = a.h0 ? a.h0[st_base + (int64_t)(r0 + r) * DV + col[j]] : 0.f;
+  float nw[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) nw[j] = EPI && a.y ? a.nw[col[j]] : 0.f;
 
   // a token's inputs, per thread: its k (threads 0-127, with g) or q
-  // element, its value column and beta (or the beta logit)
+  // element, its value columns (and gate elements), and beta (or its logit)
   struct Tok {
-    uint16_t x, v;  // raw bits: nothing waits on a load before its use
-    uint32_t b;     // the beta logit's bf16 bits, or fp32 beta's bits
+    uint16_t x, v[NC], z[NC];  // raw bits: nothing waits on a load before its use
+    uint32_t b;                // the beta logit's bf16 bits, or fp32 beta's bits
     float g;
   };
   auto load_tok = [&](int64_t t) {
@@ -104,11 +118,15 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(DecodeArgs a) {
       r.x = a.q[tok + tid - DK];
       r.g = 0.f;
     }
-    r.v = a.v[tok + col];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      r.v[j] = a.v[tok + col[j]];
+      r.z[j] = EPI && a.y ? a.z[t * a.z_stride + (int64_t)h * DK + col[j]] : 0;
+    }
     r.b = a.b ? (uint32_t)a.b[t * a.b_stride + h] : __float_as_uint(a.beta[t * a.H + h]);
     return r;
   };
-  Tok cur = {0, 0, 0u, 0.f};
+  Tok cur = {};
   if (t_beg < t_end) cur = load_tok(t_beg);
 
   for (int64_t t = t_beg; t < t_end; ++t) {
@@ -129,7 +147,6 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(DecodeArgs a) {
       const float sq = wave_sum(x * x, l);
       if (l == 0) nrm[w] = sq;
     }
-    const float vv = bf16_to_f32(cur.v);
     const float beta = a.b ? 1.f / (1.f + expf(-bf16_to_f32((uint16_t)cur.b)))
                            : __uint_as_float(cur.b);
     __syncthreads();
@@ -141,30 +158,72 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(DecodeArgs a) {
     }
 
     // decay, then this wave's part of (S^T k)[col]
-    float pu = 0.f;
+    float pu[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) pu[j] = 0.f;
 #pragma unroll
     for (int r = 0; r < DEC_ROWS; ++r) {
-      S[r] *= eg[r0 + r];
-      pu = fmaf(S[r], ks[r0 + r] * rk, pu);
+      const float e = eg[r0 + r], kr = ks[r0 + r] * rk;
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        S[j][r] *= e;
+        pu[j] = fmaf(S[j][r], kr, pu[j]);
+      }
     }
-    red[w][l] = pu;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) red[w][j * 64 + l] = pu[j];
     __syncthreads();
-    const float u = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
-    const float d = beta * (vv - u);
+    float dd[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c = j * 64 + l;
+      const float u = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+      dd[j] = beta * (bf16_to_f32(cur.v[j]) - u);
+    }
 
     // rank-one write, then this wave's part of (S^T q)[col]
-    float po = 0.f;
+    float po[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) po[j] = 0.f;
 #pragma unroll
     for (int r = 0; r < DEC_ROWS; ++r) {
-      S[r] = fmaf(ks[r0 + r] * rk, d, S[r]);
-      po = fmaf(S[r], qs[r0 + r] * rq, po);
+      const float kr = ks[r0 + r] * rk, qr = qs[r0 + r] * rq;
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        S[j][r] = fmaf(kr, dd[j], S[j][r]);
+        po[j] = fmaf(S[j][r], qr, po[j]);
+      }
     }
     __syncthreads();  // every wave has read red (u) and ks, qs, eg
-    red[w][l] = po;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) red[w][j * 64 + l] = po[j];
     __syncthreads();
     if (w == 0) {
-      const float o = a.scale * (((red[0][l] + red[1][l]) + red[2][l]) + red[3][l]);
-      a.o[tok + col] = __builtin_bit_cast(uint16_t, (__bf16)o);  // nearest even
+      float o[NC];
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const int c = j * 64 + l;
+        o[j] = a.scale * (((red[0][c] + red[1][c]) + red[2][c]) + red[3][c]);
+        a.o[tok + col[j]] = __builtin_bit_cast(uint16_t, (__bf16)o[j]);  // nearest even
+      }
+      if constexpr (EPI) {
+        if (a.y) {
+          // fused epilogue on the fp32 row: y = w * o / sqrt(mean o^2 + eps) * act(z)
+          float ss = 0.f;
+#pragma unroll
+          for (int j = 0; j < NC; ++j) ss = fmaf(o[j], o[j], ss);
+          ss = wave_sum(ss, l);
+          const float dn = ss * (1.f / DV) + a.neps;
+          const float rs = dn > 0.f ? 1.f / sqrtf(dn) : 0.f;
+#pragma unroll
+          for (int j = 0; j < NC; ++j) {
+            const float z = bf16_to_f32(cur.z[j]);
+            const float sg = 1.f / (1.f + expf(-z));
+            const float act = a.act == 0 ? sg : z * sg;
+            a.y[tok + col[j]] = __builtin_bit_cast(uint16_t, (__bf16)(nw[j] * (o[j] * rs) * act));
+          }
+        }
+      }
     }
     // the next token's staging writes come after wave 0 has read red: it
     // reaches the next barrier only after that read
@@ -173,14 +232,23 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(DecodeArgs a) {
 
   if (a.hT) {
 #pragma unroll
-    for (int r = 0; r < DEC_ROWS; ++r) a.hT[st_base + (int64_t)(r0 + r) * DV + col] = S[r];
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+      for (int r = 0; r < DEC_ROWS; ++r) a.hT[st_base + (int64_t)(r0 + r) * DV + col[j]] = S[j][r];
   }
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
-  const int64_t wgs = (int64_t)a.N * a.H * (DV / DEC_COLS);
-  if (wgs <= 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_kernel, dim3((unsigned)wgs), dim3(64 * DEC_WAVES), 0, stream, a);
+  if (a.y) {
+    const int64_t wgs = (int64_t)a.N * a.H;
+    if (wgs <= 0) return hipSuccess;
+    hipLaunchKernelGGL(decode_kernel<DV>, dim3((unsigned)wgs), dim3(64 * DEC_WAVES), 0, stream, a);
+  } else {
+    const int64_t wgs = (int64_t)a.N * a.H * (DV / DEC_COLS);
+    if (wgs <= 0) return hipSuccess;
+    hipLaunchKernelGGL(decode_kernel<DEC_COLS>, dim3((unsigned)wgs), dim3(64 * DEC_WAVES), 0, stream,
+                       a);
+  }
   return hipGetLastError();
 }
 

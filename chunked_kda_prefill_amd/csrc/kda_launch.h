@@ -65,6 +65,14 @@ struct DecodeArgs {
   const uint16_t *b;  // fused prologue, as in IntraArgs
   int64_t b_stride;
   float qk_eps;
+  // fused gated-RMSNorm epilogue when y is set: y[t, h, :] from o's fp32
+  // row, the gate row at z + t * z_stride + h * 128 and the weight nw [128]
+  uint16_t *y;
+  const uint16_t *z;
+  int64_t z_stride;
+  const float *nw;
+  float neps;
+  int32_t act;  // 0 sigmoid, 1 SiLU
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 

@@ -191,6 +191,37 @@ kda_status kda_gated_rmsnorm(const void *x, int64_t x_stride, const void *gate,
                              hipStream_t stream);
 
 /*
+ * A whole decode step of the layer in one kernel: kda_decode_fwd_fused (the
+ * prologue: beta from logits, q/k L2 norm) with kda_gated_rmsnorm applied to
+ * each output row before it leaves the chip (MI355X Kimi K3 serving post,
+ * section 1.3: the decode step fused into one kernel, output normalisation
+ * included).  The norm uses o's fp32 row (before o's bf16 rounding).
+ *
+ *   q ... scale           as in kda_decode_fwd_fused (b required when T > 0).
+ *   gate, gate_stride     bf16 gate rows as in kda_gated_rmsnorm (2-byte
+ *                         aligned; gate_stride >= H * 128).
+ *   norm_weight           fp32 [128], 4-byte aligned.
+ *   norm_eps, activation  as in kda_gated_rmsnorm.
+ *   o                     bf16 [T, H, 128], written as by kda_decode_fwd.
+ *   y                     bf16 [T, H, 128] (required when T > 0), the
+ *                         normalised output; it must not overlap any other
+ *                         argument.
+ *   final_state           as in kda_decode_fwd.
+ *
+ * One workgroup per (sequence, head) holds all 128 value columns, where
+ * kda_decode_fwd uses two.  KDA_ERR_UNSUPPORTED if N * H * 2 exceeds
+ * 2^31 - 1.
+ */
+kda_status kda_decode_step_fused(const void *q, const void *k, const void *v,
+                                 const float *g, const void *b, int64_t b_stride,
+                                 float qk_eps, const float *initial_state,
+                                 const int32_t *cu_seqlens, int64_t T, int32_t N,
+                                 int32_t H, float scale, const void *gate,
+                                 int64_t gate_stride, const float *norm_weight,
+                                 float norm_eps, int32_t activation, void *o, void *y,
+                                 float *final_state, hipStream_t stream);
+
+/*
  * Step-level entry points.  They run the steps of kda_chunk_fwd on their
  * own so that each step can be checked and timed separately; kda_chunk_fwd
  * does not call them.

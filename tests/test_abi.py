@@ -174,6 +174,35 @@ def test_gated_rmsnorm_rejects_bad_arguments():
     assert call(H=70000, xs=70000 * 128, zs=70000 * 128) == UNS
 
 
+def test_decode_step_rejects_bad_arguments():
+    # host-checked argument errors of kda_decode_step_fused (no launch is reached)
+    lib = kda.load_library()
+    A = 1 << 20
+    def call(**over):
+        a = dict(q=A, k=2 * A, v=3 * A, g=4 * A, b=5 * A, bs=2, eps=1e-6, h0=None, cu=6 * A,
+                 T=16, N=1, H=2, scale=1.0, z=7 * A, zs=256, nw=8 * A, neps=1e-6, act=0,
+                 o=9 * A, y=10 * A, hT=11 * A)
+        a.update(over)
+        return lib.kda_decode_step_fused(a["q"], a["k"], a["v"], a["g"], a["b"], a["bs"],
+                                         a["eps"], a["h0"], a["cu"], a["T"], a["N"], a["H"],
+                                         a["scale"], a["z"], a["zs"], a["nw"], a["neps"],
+                                         a["act"], a["o"], a["y"], a["hT"], None)
+    INV = 1
+    assert call(y=None) == INV                      # y required when T > 0
+    assert call(b=None) == INV
+    assert call(z=None) == INV
+    assert call(nw=None) == INV
+    assert call(act=5) == INV
+    assert call(neps=-1.0) == INV
+    assert call(neps=float("nan")) == INV
+    assert call(zs=255) == INV                      # below H * 128
+    assert call(z=7 * A + 1) == INV                 # misaligned gate
+    assert call(nw=8 * A + 2) == INV                # misaligned weight
+    assert call(y=9 * A + 64) == INV                # y overlaps o
+    assert call(y=7 * A) == INV                     # y is the gate
+    assert call(y=11 * A) == INV                    # y overlaps the state
+
+
 def test_python_wrapper_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "_lib", None)
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))

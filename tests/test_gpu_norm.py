@@ -148,3 +148,74 @@ def test_gated_rmsnorm_rejects_bad_views(dev):
         kda.gated_rmsnorm(x, x, w, activation="relu")
     with pytest.raises(kda.KDAError):            # slice at an offset of 4 elements: misaligned
         kda.gated_rmsnorm(x, wide[:, 4:4 + 256].view(4, 2, 128), w)
+
+
+@pytest.mark.parametrize("users,tokens,H", [(16, 1, 12), (16, 4, 12), (5, 9, 3)],
+                         ids=["decode16x1_h12", "verify16x4_h12", "5x9_h3"])
+@pytest.mark.parametrize("act", ["sigmoid", "silu"])
+def test_decode_step_fused(dev, users, tokens, H, act):
+    # the whole decode step in one kernel: o and the state bitwise equal to
+    # kda_decode_fwd_fused (the same per-column arithmetic and reduction
+    # order), y against the oracle's chain row by row
+    import torch
+    import chunked_kda_prefill_amd as kda
+    w = wl.decode_step(users, tokens, H)
+    T = w.T
+    rq, rk, bfull, pre = wl.raw_prologue_inputs(w, 302)
+    _, zf, wn, (_, pz) = _inputs(T, H, seed=412)
+    t = wl.to_torch(w, dev)
+    q, k = _bf(rq, dev), _bf(rk, dev)
+    b = _bf(bfull, dev)[:, pre:pre + H]
+    z = _bf(zf, dev)[:, pz:pz + H * 128].view(T, H, 128)
+    wt = torch.from_numpy(wn).to(dev)
+    log(f"[case] decode_step_fused {users}x{tokens} H={H} act={act}")
+    o, y, f = kda.decode_step_fused(q, k, t["v"], t["g"], b, t["cu_seqlens"], z, wt,
+                                    initial_state=t["initial_state"], scale=1.0, activation=act)
+    o2, f2 = kda.decode_fwd_fused(q, k, t["v"], t["g"], b, t["cu_seqlens"],
+                                  initial_state=t["initial_state"], scale=1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(f, f2)
+    qn, kn, beta = oracle.prologue(rq, rk, bfull[:, pre:pre + H], qk_eps=1e-6)
+    o_ref, f_ref = oracle.kda_fwd(qn, kn, w.v, w.g, beta, w.cu_seqlens, w.initial_state,
+                                  scale=1.0)
+    o_gpu = wl.bf16_tensor_to_f32(o).astype(np.float64)
+    eo = oracle.max_abs_err(o_gpu, o_ref), oracle.rel_fro_err(o_gpu, o_ref)
+    assert eo[0] <= MAX_ABS and eo[1] <= REL_FRO, eo
+    z_ref = zf[:, pz:pz + H * 128].reshape(T, H, 128)
+    y_all = oracle.gated_rmsnorm(o_ref, z_ref, wn, 1e-6, act)
+    zz = wl.bf16_bits_to_f32(z_ref).astype(np.float64)
+    sig = 1.0 / (1.0 + np.exp(-zz))
+    dmax = np.abs(wn * (sig if act == "sigmoid" else zz * sig)).max(axis=-1)
+    d = np.linalg.norm(wl.bf16_tensor_to_f32(y).astype(np.float64) - y_all, axis=-1)
+    # the kernel normalises o's fp32 row; the bf16 o read back is within
+    # 2^-8 of it per row, so e_o of the fp32 row <= e_o(bf16) + 2^-8
+    e_o = np.linalg.norm(o_gpu - o_ref, axis=-1) / np.linalg.norm(o_ref, axis=-1)
+    bound = dmax * np.sqrt(128.0) * (2.0 * (e_o + 2.0 ** -8) + 2.0 ** -8) + 1e-5
+    log(f"[parity] decode step y rows: max |y - y_ref| / bound = {(d / bound).max():.3f}, "
+        f"y relF {oracle.rel_fro_err(wl.bf16_tensor_to_f32(y).astype(np.float64), y_all):.3e}")
+    assert np.all(np.isfinite(d)) and np.all(d <= bound)
+
+
+def test_decode_step_fused_varlen_empty(dev):
+    import torch
+    import chunked_kda_prefill_amd as kda
+    w = wl.small([0, 1, 2, 0, 3, 5, 8, 4], H=3, seed=76)
+    T, H = w.T, w.H
+    rq, rk, bfull, pre = wl.raw_prologue_inputs(w, 303)
+    _, zf, wn, (_, pz) = _inputs(T, H, seed=413)
+    t = wl.to_torch(w, dev)
+    q, k, b = _bf(rq, dev), _bf(rk, dev), _bf(bfull, dev)[:, pre:pre + H]
+    z = _bf(zf, dev)[:, pz:pz + H * 128].view(T, H, 128)
+    log("[case] decode_step_fused varlen with empty sequences")
+    o, y, f = kda.decode_step_fused(q, k, t["v"], t["g"], b, t["cu_seqlens"], z,
+                                    torch.from_numpy(wn).to(dev),
+                                    initial_state=t["initial_state"])
+    o2, f2 = kda.decode_fwd_fused(q, k, t["v"], t["g"], b, t["cu_seqlens"],
+                                  initial_state=t["initial_state"])
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(f, f2)
+    ff = f.cpu().numpy()
+    for s in (0, 3):
+        assert np.array_equal(ff[s], w.initial_state[s])
+    assert np.all(np.isfinite(wl.bf16_tensor_to_f32(y)))
