@@ -20,7 +20,7 @@
 // four waves' partial sums added in LDS in a fixed order, so results are
 // deterministic.  State loads and stores are 256-byte row segments per wave.
 #include "kda_internal.h"
-#include "kda_launch.h"
+#include "kda_decode.h"
 
 namespace kda {
 

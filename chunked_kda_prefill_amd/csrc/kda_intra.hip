@@ -47,7 +47,7 @@
 #include "kda_chunk_table.h"
 #include "kda_cumsum.h"
 #include "kda_internal.h"
-#include "kda_launch.h"
+#include "kda_intra.h"
 
 namespace kda {
 

@@ -18,7 +18,7 @@
 // x rows, z rows and y rows are 256 contiguous bytes each, so every access
 // is a full 256-byte segment.
 #include "kda_internal.h"
-#include "kda_launch.h"
+#include "kda_norm.h"
 
 namespace kda {
 

@@ -16,7 +16,7 @@
 // is what bounds a chain; the split is picked at launch so that the
 // workgroups still fit the device once each.
 #include "kda_internal.h"
-#include "kda_launch.h"
+#include "kda_recurrence.h"
 
 namespace kda {
 
