@@ -109,3 +109,12 @@ def test_fused_rejects_bad_logits(dev):
             kda.chunk_fwd_fused(*args, bad, t["cu_seqlens"])
         with pytest.raises(ValueError):
             kda.decode_fwd_fused(*args, bad, t["cu_seqlens"])
+
+
+def test_chunk_fused_many_sequences(dev):
+    # past 1,024 sequences a separate kernel builds the chunk table: the
+    # fused prologue on that side of the switch too
+    lens = list(np.random.default_rng(6).integers(0, 140, size=1100))
+    w = wl.make_workload("fused_many_N1100", lens, H=2, seed=77, h0="normal")
+    log(f"[case] chunk_fwd_fused N=1100 T={w.T}")
+    parity(*run_fused(w, dev), "chunk fused N=1100")

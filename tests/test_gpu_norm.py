@@ -219,3 +219,35 @@ def test_decode_step_fused_varlen_empty(dev):
     for s in (0, 3):
         assert np.array_equal(ff[s], w.initial_state[s])
     assert np.all(np.isfinite(wl.bf16_tensor_to_f32(y)))
+
+
+def test_decode_step_fused_empty_batch_and_no_norm(dev):
+    # T = 0: the states pass through; qk_eps None: q and k as given
+    import torch
+    import chunked_kda_prefill_amd as kda
+    H = 2
+    e = torch.zeros((0, H, 128), dtype=torch.bfloat16, device=dev)
+    eg = torch.zeros((0, H, 128), dtype=torch.float32, device=dev)
+    eb = torch.zeros((0, H), dtype=torch.bfloat16, device=dev)
+    cu = torch.zeros(3, dtype=torch.int32, device=dev)
+    h0 = torch.randn((2, H, 128, 128), device=dev)
+    wt = torch.ones(128, dtype=torch.float32, device=dev)
+    log("[case] decode_step_fused T=0")
+    o, y, f = kda.decode_step_fused(e, e, e, eg, eb, cu, e, wt, initial_state=h0)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0 and y.shape[0] == 0 and torch.equal(f, h0)
+    w = wl.decode_step(8, 2, 2)
+    T = w.T
+    _, zf, wn, (_, pz) = _inputs(T, 2, seed=414)
+    rq, rk, bfull, pre = wl.raw_prologue_inputs(w, 304)
+    t = wl.to_torch(w, dev)
+    b = _bf(bfull, dev)[:, pre:pre + 2]
+    z = _bf(zf, dev)[:, pz:pz + 256].view(T, 2, 128)
+    log("[case] decode_step_fused qk_eps=None")
+    o, y, f = kda.decode_step_fused(t["q"], t["k"], t["v"], t["g"], b, t["cu_seqlens"], z,
+                                    torch.from_numpy(wn).to(dev),
+                                    initial_state=t["initial_state"], qk_eps=None)
+    o2, f2 = kda.decode_fwd_fused(t["q"], t["k"], t["v"], t["g"], b, t["cu_seqlens"],
+                                  initial_state=t["initial_state"], qk_eps=None)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(f, f2)
