@@ -56,6 +56,8 @@ def parse():
                     help="run a plain device copy of this size first (counter scale)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line: per-config latency table (markdown)")
+    ap.add_argument("--only", default="",
+                    help="with --sweep: a comma-separated subset of the sweep's config names")
     return ap.parse_args()
 
 
@@ -128,8 +130,13 @@ def sweep(args, torch, np, kda, wl):
     print("| config | T | N | H | chunks | median µs | p10 µs | p90 µs | M tokens/s | GB/s | "
           "HBM frac | TFLOP/s | oracle tokens/s (heads) | GPU/oracle |")
     print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+    only = [x for x in args.only.split(",") if x]
+    unknown = [x for x in only if x not in SWEEP_CONFIGS]
+    if unknown:
+        raise SystemExit(f"--only: not sweep configs: {unknown} (known: {SWEEP_CONFIGS})")
+    configs = [n for n in SWEEP_CONFIGS if not only or n in only]
     runs = []
-    for n in SWEEP_CONFIGS:
+    for n in configs:
         main = ["decode_fwd", "chunk_fwd"] if n.startswith("decode") else ["chunk_fwd"]
         if n in FUSED_SWEEP_CONFIGS:
             main = main + [e + "_fused" for e in main] + ["torch prologue + " + main[0]]
@@ -219,17 +226,17 @@ def sweep(args, torch, np, kda, wl):
         del t, ws, o, fin
         if fused:
             del blog
-    norm_sweep(torch, np, kda, wl, dev, stream, flush, sink)
+    norm_sweep(torch, np, kda, wl, dev, stream, flush, sink, configs)
 
 
-def norm_sweep(torch, np, kda, wl, dev, stream, flush, sink):
+def norm_sweep(torch, np, kda, wl, dev, stream, flush, sink, configs):
     """Cold latency of the gated-RMSNorm epilogue (kda_gated_rmsnorm) at the
     output shapes of FUSED_SWEEP_CONFIGS: x = o [T, H, 128] contiguous, the
     gate a column slice of a [T, H*128 + 128] bf16 tensor.  Algorithmic bytes
     per (token, head) row: 256 read of x, 256 of the gate, 256 written."""
     print("\n| epilogue config | T | H | median µs | p10 µs | p90 µs | GB/s | HBM frac |")
     print("|---|---|---|---|---|---|---|---|")
-    for name in FUSED_SWEEP_CONFIGS:
+    for name in [n for n in FUSED_SWEEP_CONFIGS if n in configs]:
         w = wl.by_name(name)
         T, H = w.T, w.H
         x = torch.randn((T, H, 128), device=dev).to(torch.bfloat16)
