@@ -286,7 +286,8 @@ static kda_status decode_fwd_impl(const void *q, const void *k, const void *v, c
     if (!(epi.eps >= 0.f) || epi.eps == INFINITY) return KDA_ERR_INVALID_ARGUMENT;
     if (epi.act != KDA_ACT_SIGMOID && epi.act != KDA_ACT_SILU) return KDA_ERR_INVALID_ARGUMENT;
     const int64_t row = (int64_t)H * DK;
-    if (epi.z_stride < row || epi.z_stride > ((int64_t)1 << 40)) return KDA_ERR_INVALID_ARGUMENT;
+    // up to 2^31 elements: (T - 1) * z_stride (T < 2^31) stays inside int64
+    if (epi.z_stride < row || epi.z_stride > ((int64_t)1 << 31)) return KDA_ERR_INVALID_ARGUMENT;
     const int64_t zbytes = ((T - 1) * epi.z_stride + row) * 2;
     const int64_t st_bytes = (int64_t)N * H * DK * DV * 4;
     // y is written: it overlaps nothing else the call reads or writes
@@ -412,8 +413,9 @@ kda_status kda_gated_rmsnorm(const void *x, int64_t x_stride, const void *gate,
   if (!aligned(x, 16) || !aligned(gate, 16) || !aligned(weight, 16) || !aligned(y, 16))
     return KDA_ERR_INVALID_ARGUMENT;
   // 16-byte row segments: strides are whole multiples of 8 elements
+  // strides up to 2^31 elements keep (T - 1) * stride (T < 2^31) inside int64
   if (x_stride < row || gate_stride < row || x_stride % 8 || gate_stride % 8 ||
-      x_stride > ((int64_t)1 << 40) || gate_stride > ((int64_t)1 << 40))
+      x_stride > ((int64_t)1 << 31) || gate_stride > ((int64_t)1 << 31))
     return KDA_ERR_INVALID_ARGUMENT;
   const int64_t ybytes = T * row * 2;
   const int64_t xbytes = ((T - 1) * x_stride + row) * 2;

@@ -172,9 +172,9 @@ kda_status kda_decode_fwd_fused(const void *q, const void *k, const void *v,
  * row with eps = 0 stays zero.
  *
  *   x, gate   bf16; row (t, h) at element t * stride + h * 128, with
- *             x_stride, gate_stride >= H * 128 and multiples of 8 (16-byte
- *             row segments), e.g. column slices of a row-major [T, stride]
- *             tensor.  16-byte aligned.
+ *             H * 128 <= x_stride, gate_stride <= 2^31, multiples of 8
+ *             (16-byte row segments), e.g. column slices of a row-major
+ *             [T, stride] tensor.  16-byte aligned.
  *   weight    fp32 [128], 16-byte aligned.
  *   eps       >= 0 and finite.
  *   y         bf16 [T, H, 128] contiguous, 16-byte aligned.  y == x (with
@@ -199,7 +199,7 @@ kda_status kda_gated_rmsnorm(const void *x, int64_t x_stride, const void *gate,
  *
  *   q ... scale           as in kda_decode_fwd_fused (b required when T > 0).
  *   gate, gate_stride     bf16 gate rows as in kda_gated_rmsnorm (2-byte
- *                         aligned; gate_stride >= H * 128).
+ *                         aligned; H * 128 <= gate_stride <= 2^31).
  *   norm_weight           fp32 [128], 4-byte aligned.
  *   norm_eps, activation  as in kda_gated_rmsnorm.
  *   o                     bf16 [T, H, 128], written as by kda_decode_fwd.

@@ -168,6 +168,7 @@ def test_gated_rmsnorm_rejects_bad_arguments():
     assert call(eps=float("inf")) == INV
     assert call(xs=255) == INV                            # below H * 128
     assert call(zs=260) == INV                            # not a multiple of 8
+    assert call(xs=(1 << 31) + 8) == INV                  # stride beyond 2^31
     assert call(z=2 * A + 8) == INV                       # misaligned
     assert call(y=A + 512) == INV                         # y overlaps x (not in place)
     assert call(y=2 * A) == INV                           # y is the gate
@@ -196,6 +197,7 @@ def test_decode_step_rejects_bad_arguments():
     assert call(neps=-1.0) == INV
     assert call(neps=float("nan")) == INV
     assert call(zs=255) == INV                      # below H * 128
+    assert call(zs=(1 << 31) + 8) == INV            # beyond 2^31
     assert call(z=7 * A + 1) == INV                 # misaligned gate
     assert call(nw=8 * A + 2) == INV                # misaligned weight
     assert call(y=9 * A + 64) == INV                # y overlaps o
