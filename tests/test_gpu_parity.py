@@ -41,12 +41,24 @@ def test_edge_lengths(dev, pinned):
     parity(o, f, o_ref, f_ref, f"edge pinned={pinned}")
 
 
-def test_heads_1_and_8(dev):
-    for H in (1, 8):
+def test_heads_1_8_and_32(dev):
+    # H = 32 also gives 96 chains, where the recurrence splits each chain
+    # over two workgroups instead of four
+    for H in (1, 8, 32):
         w = wl.small([100, 64, 3], H=H, seed=42)
         log(f"[case] H={H}")
         o, f = run_gpu(w, dev)
         parity(o, f, *run_oracle(w), f"H={H}")
+
+
+def test_sampled_lengths(dev):
+    # the eight sampled sequence lengths of the KDA TPU report's correctness
+    # section: short, sub-subblock, exact multiples of 16 and 64, and long
+    w = wl.make_workload("sampled8", [53, 14, 13, 33, 16, 480, 512, 77], H=4, seed=45,
+                         h0="normal")
+    log("[case] sampled lengths")
+    o, f = run_gpu(w, dev)
+    parity(o, f, *run_oracle(w), "sampled lengths")
 
 
 def test_headline(dev):
