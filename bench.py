@@ -266,9 +266,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {max(args.gpus, world)}); "
-              "the KDA prefill path shards by heads or sequences with no exchange, "
-              "see DESIGN.md", file=sys.stderr)
+        print(f"bench.py: this library runs on one GPU only (asked for "
+              f"{max(args.gpus, world)}); the KDA prefill path would shard by heads or by "
+              "sequences, with no exchange inside the operation", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
