@@ -14,7 +14,7 @@ Inputs are resident in HBM before timing starts.  Several device copies of
 the inputs are rotated so that every step reads inputs that are not left in
 the 256 MB Infinity Cache by the previous step.
 
-Prints ONE JSON line.  ``--gpus`` above 1 exits: this build runs on one GPU.
+Prints ONE JSON line.  ``--gpus`` above 1 exits: the library runs on one GPU.
 """
 
 from __future__ import annotations
