@@ -106,6 +106,11 @@ def sweep(args, torch, np, kda, wl):
     and with that prologue done by torch ops before the plain entry point;
     their decode configs also as a whole decode step with the gated RMSNorm
     (kda_decode_step_fused, and kda_decode_fwd_fused + kda_gated_rmsnorm)."""
+    only = [x for x in args.only.split(",") if x]
+    unknown = [x for x in only if x not in SWEEP_CONFIGS]
+    if unknown:
+        raise SystemExit(f"--only: not sweep configs: {unknown} (known: {SWEEP_CONFIGS})")
+    configs = [n for n in SWEEP_CONFIGS if not only or n in only]
     import oracle
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
@@ -130,11 +135,6 @@ def sweep(args, torch, np, kda, wl):
     print("| config | T | N | H | chunks | median µs | p10 µs | p90 µs | M tokens/s | GB/s | "
           "HBM frac | TFLOP/s | oracle tokens/s (heads) | GPU/oracle |")
     print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
-    only = [x for x in args.only.split(",") if x]
-    unknown = [x for x in only if x not in SWEEP_CONFIGS]
-    if unknown:
-        raise SystemExit(f"--only: not sweep configs: {unknown} (known: {SWEEP_CONFIGS})")
-    configs = [n for n in SWEEP_CONFIGS if not only or n in only]
     runs = []
     for n in configs:
         main = ["decode_fwd", "chunk_fwd"] if n.startswith("decode") else ["chunk_fwd"]
