@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     gated_rmsnorm,
     load_library,
     new_workspace,
+    validate_inputs,
     workspace_layout,
     workspace_size,
 )

@@ -27,7 +27,8 @@ EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd"
             "kda_chunk_table", "kda_gate_cumsum", "kda_chunk_intra",
             "kda_workspace_layout", "kda_chunk_recurrence", "kda_decode_fwd",
             "kda_chunk_fwd_fused", "kda_decode_fwd_fused", "kda_gated_rmsnorm",
-            "kda_decode_step_fused")
+            "kda_decode_step_fused", "kda_validate_inputs")
+VALIDATION_BITS = {1: "cu_seqlens", 2: "g", 4: "beta"}
 ACTIVATIONS = {"sigmoid": 0, "silu": 1}
 
 
@@ -70,6 +71,8 @@ def load_library():
     lib.kda_decode_step_fused.argtypes = [P, P, P, P, P, I64, F32, P, P, I64, I32, I32, F32,
                                           P, I64, P, F32, I32, P, P, P, P]
     lib.kda_decode_step_fused.restype = ctypes.c_int
+    lib.kda_validate_inputs.argtypes = [P, P, P, I64, I32, I32, P, P]
+    lib.kda_validate_inputs.restype = ctypes.c_int
     lib.kda_chunk_table.argtypes = [P, I64, I32, P, P, P, P]
     lib.kda_chunk_table.restype = ctypes.c_int
     lib.kda_gate_cumsum.argtypes = [P, P, I64, I32, I32, P, P, SZ, P]
@@ -362,6 +365,28 @@ def decode_step_fused(q, k, v, g, b, cu_seqlens, gate, norm_weight, initial_stat
         ACTIVATIONS[activation], _ptr(o), _ptr(y), _ptr(final_state), _stream(q.device))
     _check("kda_decode_step_fused", st)
     return o, y, final_state
+
+
+def validate_inputs(g, beta, cu_seqlens):
+    """Opt-in check of the device-content contracts (kda_validate_inputs):
+    returns the set of failed checks, a subset of {"cu_seqlens", "g",
+    "beta"} (empty when all hold).  beta may be None.  Synchronises the
+    current stream to read the result."""
+    torch = _torch()
+    _expect(cu_seqlens, "cu_seqlens", torch.int32)
+    _expect(g, "g", torch.float32)
+    if g.dim() != 3 or g.shape[2] != HEAD_DIM:
+        raise ValueError("g must be fp32 [T, H, 128]")
+    T, H = int(g.shape[0]), int(g.shape[1])
+    if beta is not None:
+        _expect(beta, "beta", torch.float32, (T, H))
+    N = int(cu_seqlens.shape[0]) - 1
+    flags = torch.empty(1, dtype=torch.int32, device=g.device)
+    st = load_library().kda_validate_inputs(_ptr(g), _ptr(beta), _ptr(cu_seqlens), T, N, H,
+                                            _ptr(flags), _stream(g.device))
+    _check("kda_validate_inputs", st)
+    word = int(flags.item())
+    return {name for bit, name in VALIDATION_BITS.items() if word & bit}
 
 
 def chunk_table(cu_seqlens, T: int):

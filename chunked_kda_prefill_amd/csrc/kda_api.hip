@@ -398,6 +398,30 @@ kda_status kda_decode_step_fused(const void *q, const void *k, const void *v, co
                          final_state, stream, pro, epi);
 }
 
+kda_status kda_validate_inputs(const float *g, const float *beta, const int32_t *cu_seqlens,
+                               int64_t T, int32_t N, int32_t H, int32_t *flags,
+                               hipStream_t stream) {
+  kda_status st = check_sizes(T, N, H);
+  if (st != KDA_OK) return st;
+  if (!cu_seqlens || !flags || !aligned(cu_seqlens, 4) || !aligned(flags, 4))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!g || !aligned(g, 16))) return KDA_ERR_INVALID_ARGUMENT;
+  if (beta && !aligned(beta, 4)) return KDA_ERR_INVALID_ARGUMENT;
+  const int64_t tok = T * H * DK;
+  if (overlap(flags, 4, g, tok * 4) || overlap(flags, 4, beta, T * H * 4) ||
+      overlap(flags, 4, cu_seqlens, ((int64_t)N + 1) * 4))
+    return KDA_ERR_INVALID_ARGUMENT;
+  ValidateArgs va;
+  va.g = g;
+  va.beta = T > 0 ? beta : nullptr;
+  va.cu = cu_seqlens;
+  va.flags = flags;
+  va.T = T;
+  va.N = N;
+  va.H = H;
+  return hip_status(launch_validate(va, stream));
+}
+
 kda_status kda_gated_rmsnorm(const void *x, int64_t x_stride, const void *gate,
                              int64_t gate_stride, const float *weight, float eps,
                              int32_t activation, int64_t T, int32_t H, void *y,

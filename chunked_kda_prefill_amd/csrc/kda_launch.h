@@ -11,6 +11,7 @@
 #include "kda_intra.h"
 #include "kda_norm.h"
 #include "kda_recurrence.h"
+#include "kda_validate.h"
 
 namespace kda {
 

@@ -222,6 +222,23 @@ kda_status kda_decode_step_fused(const void *q, const void *k, const void *v,
                                  float *final_state, hipStream_t stream);
 
 /*
+ * Opt-in check of the contracts on device contents that the entry points
+ * above trust (they never read out of bounds on any input, but compute
+ * garbage on a broken contract): cu_seqlens monotone with cu[0] = 0 and
+ * cu[N] = T; every g inside [-5, 0] (the KDA TPU report's lower bound,
+ * section 4); every beta inside [0, 1] (beta may be NULL: not checked).
+ * NaN fails both range checks.  Enqueued on `stream`: a kernel clears
+ * *flags, a second ORs in KDA_BAD_CU_SEQLENS, KDA_BAD_G and KDA_BAD_BETA
+ * for what it finds; read *flags after the stream has run.  flags: device
+ * int32 [1], 4-byte aligned, not overlapping the inputs.  g: 16-byte
+ * aligned.  Not part of any forward call; it reads g once more.
+ */
+enum { KDA_BAD_CU_SEQLENS = 1, KDA_BAD_G = 2, KDA_BAD_BETA = 4 };
+kda_status kda_validate_inputs(const float *g, const float *beta,
+                               const int32_t *cu_seqlens, int64_t T, int32_t N,
+                               int32_t H, int32_t *flags, hipStream_t stream);
+
+/*
  * Step-level entry points.  They run the steps of kda_chunk_fwd on their
  * own so that each step can be checked and timed separately; kda_chunk_fwd
  * does not call them.

@@ -205,6 +205,24 @@ def test_decode_step_rejects_bad_arguments():
     assert call(y=11 * A) == INV                    # y overlaps the state
 
 
+def test_validate_rejects_bad_arguments():
+    # host-checked argument errors of kda_validate_inputs (no launch is reached)
+    lib = kda.load_library()
+    A = 1 << 20
+    def call(**over):
+        a = dict(g=A, beta=2 * A, cu=3 * A, T=16, N=1, H=2, flags=4 * A)
+        a.update(over)
+        return lib.kda_validate_inputs(a["g"], a["beta"], a["cu"], a["T"], a["N"], a["H"],
+                                       a["flags"], None)
+    INV = 1
+    assert call(flags=None) == INV
+    assert call(cu=None) == INV
+    assert call(g=None) == INV
+    assert call(g=A + 4) == INV                     # g not 16-byte aligned
+    assert call(flags=A + 64) == INV                # flags inside g
+    assert call(N=0) == INV
+
+
 def test_python_wrapper_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "_lib", None)
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
