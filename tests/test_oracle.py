@@ -316,3 +316,21 @@ def test_gated_rmsnorm_closed_forms():
     assert np.allclose(ye[..., 5], 2.0 * y[..., 5], rtol=1e-14, atol=0)
     zr = oracle.gated_rmsnorm(np.zeros((2, 1, 128)), big[:2, :1], w1, 0.0)
     assert np.array_equal(zr, np.zeros((2, 1, 128)))
+
+
+def test_norms_reduce_to_library_routines():
+    # with an open gate (sigmoid = 1 in fp64) the gated RMSNorm is torch's
+    # rms_norm; with eps = 0 the prologue's L2 norm is torch's normalize
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(24)
+    x = rng.normal(size=(7, 3, 128)) * rng.uniform(0.05, 20, size=(7, 3, 1))
+    w = rng.uniform(-2, 2, size=128)
+    for eps in (0.0, 1e-6, 0.3):
+        y = oracle.gated_rmsnorm(x, np.full_like(x, 40.0), w, eps)
+        ref = F.rms_norm(torch.from_numpy(x), (128,), weight=torch.from_numpy(w), eps=eps)
+        assert np.allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12), eps
+    qn, kn, _ = oracle.prologue(x, 3.0 * x, np.zeros((7, 3)), qk_eps=0.0)
+    ref = F.normalize(torch.from_numpy(x), dim=-1, eps=0.0).numpy()
+    assert np.allclose(qn, ref, rtol=1e-13, atol=1e-15)
+    assert np.allclose(kn, ref, rtol=1e-13, atol=1e-15)
