@@ -334,3 +334,63 @@ def test_norms_reduce_to_library_routines():
     ref = F.normalize(torch.from_numpy(x), dim=-1, eps=0.0).numpy()
     assert np.allclose(qn, ref, rtol=1e-13, atol=1e-15)
     assert np.allclose(kn, ref, rtol=1e-13, atol=1e-15)
+
+
+def test_widen_matches_torch_bfloat16_conversion():
+    # oracle.widen turns bf16 bit patterns into fp32.  Pinned against torch's
+    # own bfloat16 -> float32 conversion over every one of the 65,536 bit
+    # patterns, and against values fixed by the bf16 format itself (sign,
+    # 8-bit exponent, 7-bit mantissa): 0x3F80 = 1, 0xC000 = -2, 0x3F81 =
+    # 1 + 2^-7, 0x0001 = 2^-133 (smallest subnormal), 0x7F80 = +inf.
+    import torch
+    bits = np.arange(65536, dtype=np.uint16)
+    got = oracle.widen(bits)
+    assert got.dtype == np.float32
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    same = (got.view(np.uint32) == ref.view(np.uint32)) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+    fixed = oracle.widen(np.array([0x3F80, 0xC000, 0x3F81, 0x0001, 0x7F80, 0x8000], np.uint16))
+    assert fixed[0] == 1.0 and fixed[1] == -2.0 and fixed[2] == 1.0 + 2.0 ** -7
+    assert fixed[3] == 2.0 ** -133 and np.isposinf(fixed[4])
+    assert fixed[5] == 0.0 and np.signbit(fixed[5])
+    # float arrays pass through unchanged
+    f = np.array([0.1, -3.5], np.float32)
+    assert oracle.widen(f) is f
+
+
+def test_bf16_bit_inputs_equal_their_float_values():
+    # the GPU parity tests hand the oracle bf16 bit patterns: the run must
+    # equal the run on the same values given as floats (bitwise)
+    import torch
+    rng = np.random.default_rng(25)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [70, 0, 33], H=2, dk=128, dv=128)
+
+    def to_bits(x):
+        t = torch.from_numpy(x).to(torch.bfloat16)
+        return t.view(torch.int16).numpy().view(np.uint16), t.float().numpy()
+
+    (qb, qf), (kb, kf), (vb, vf) = to_bits(q), to_bits(k), to_bits(v)
+    o1, f1 = oracle.kda_fwd(qb, kb, vb, g, beta, cu, S0)
+    o2, f2 = oracle.kda_fwd(qf, kf, vf, g, beta, cu, S0)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+
+
+def test_head_sampling_equals_columns_of_the_full_run():
+    # kda_fwd(heads=...) is the reference of every sampled-head GPU parity
+    # test: it must give exactly the matching head columns of the full run,
+    # in the order asked for, with and without an initial state
+    rng = np.random.default_rng(26)
+    q, k, v, g, beta, cu, S0 = rand_inputs(rng, [45, 0, 80, 3], H=6, dk=128, dv=128)
+    for h0 in (S0, None):
+        o, f = oracle.kda_fwd(q, k, v, g, beta, cu, h0, scale=0.9)
+        for heads in ([4], [5, 0, 2], [1, 1]):
+            os_, fs = oracle.kda_fwd(q, k, v, g, beta, cu, h0, scale=0.9, heads=heads)
+            assert os_.shape == (q.shape[0], len(heads), 128)
+            assert fs.shape == (len(cu) - 1, len(heads), 128, 128)
+            assert np.array_equal(os_, o[:, heads]) and np.array_equal(fs, f[:, heads])
+    # a head's result does not depend on the other heads' inputs
+    q2 = q.copy()
+    q2[:, 3] += 1.0
+    o3, f3 = oracle.kda_fwd(q2, k, v, g, beta, cu, S0, heads=[0, 5])
+    o4, f4 = oracle.kda_fwd(q, k, v, g, beta, cu, S0, heads=[0, 5])
+    assert np.array_equal(o3, o4) and np.array_equal(f3, f4)
