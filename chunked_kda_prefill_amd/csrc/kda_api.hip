@@ -74,6 +74,41 @@ kda_status check_inputs(const void *q, const void *k, const void *v, const float
 
 kda_status hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
+// The device regions a forward call reads: q, k, v, g, beta (or the beta
+// logits b of a strided slice), cu_seqlens and the initial state.
+struct Inputs {
+  const void *p[8];
+  int64_t bytes[8];
+  int n = 0;
+  void add(const void *ptr, int64_t b) {
+    p[n] = ptr;
+    bytes[n] = b;
+    ++n;
+  }
+  // does [w, w + wbytes) overlap any of them?
+  bool hit(const void *w, int64_t wbytes) const {
+    for (int i = 0; i < n; ++i)
+      if (overlap(w, wbytes, p[i], bytes[i])) return true;
+    return false;
+  }
+};
+
+Inputs forward_inputs(const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, const float *initial_state, const int32_t *cu,
+                      int64_t T, int32_t N, int32_t H, const uint16_t *b, int64_t b_stride) {
+  const int64_t tok = T * H * DK;
+  Inputs in;
+  in.add(q, tok * 2);
+  in.add(k, tok * 2);
+  in.add(v, tok * 2);
+  in.add(g, tok * 4);
+  in.add(beta, T * H * 4);
+  if (b && T > 0) in.add(b, ((T - 1) * b_stride + H) * 2);
+  in.add(cu, ((int64_t)N + 1) * 4);
+  in.add(initial_state, (int64_t)N * H * DK * DV * 4);
+  return in;
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,6 +164,11 @@ kda_status kda_gate_cumsum(const float *g, const int32_t *cu_seqlens, int64_t T,
   if (overlap(G, T * H * DK * 4, g, T * H * DK * 4)) return KDA_ERR_INVALID_ARGUMENT;
   Ws ws;
   if ((st = carve(workspace, workspace_bytes, T, N, H, ws)) != KDA_OK) return st;
+  if (overlap(workspace, ws.L.total, g, T * H * DK * 4) ||
+      overlap(workspace, ws.L.total, G, T * H * DK * 4) ||
+      overlap(workspace, ws.L.total, cu_seqlens, ((int64_t)N + 1) * 4) ||
+      overlap(G, T * H * DK * 4, cu_seqlens, ((int64_t)N + 1) * 4))
+    return KDA_ERR_INVALID_ARGUMENT;
   hipError_t e = launch_chunk_table(cu_seqlens, T, N, ws.L.nc_max, ws.chunk_first, ws.chunk_info,
                                     ws.flags, stream);
   if (e != hipSuccess) return KDA_ERR_HIP;
@@ -221,6 +261,9 @@ kda_status kda_chunk_intra(const void *q, const void *k, const void *v, const fl
   if ((st = check_inputs(q, k, v, g, beta, cu_seqlens, T)) != KDA_OK) return st;
   Ws ws;
   if ((st = carve(workspace, workspace_bytes, T, N, H, ws)) != KDA_OK) return st;
+  if (forward_inputs(q, k, v, g, beta, nullptr, cu_seqlens, T, N, H, nullptr, 0)
+          .hit(workspace, ws.L.total))
+    return KDA_ERR_INVALID_ARGUMENT;
   return run_intra(q, k, v, g, beta, cu_seqlens, T, N, H, scale, ws, stream);
 }
 
@@ -236,15 +279,17 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
   if ((st = check_outputs(initial_state, T, N, H, o, final_state)) != KDA_OK) return st;
   const int64_t tok = T * H * DK;
   const int64_t st_bytes = (int64_t)N * H * DK * DV * 4;
-  // o must not alias any input
-  if (overlap(o, tok * 2, q, tok * 2) || overlap(o, tok * 2, k, tok * 2) ||
-      overlap(o, tok * 2, v, tok * 2) || overlap(o, tok * 2, g, tok * 4) ||
-      overlap(o, tok * 2, beta, T * H * 4) ||
-      (pro.b && overlap(o, tok * 2, pro.b, ((T - 1) * pro.b_stride + H) * 2)))
-    return KDA_ERR_INVALID_ARGUMENT;
+  const Inputs in = forward_inputs(q, k, v, g, beta, initial_state, cu_seqlens, T, N, H, pro.b,
+                                   pro.b_stride);
+  const Inputs in_no_h0 = forward_inputs(q, k, v, g, beta, nullptr, cu_seqlens, T, N, H, pro.b,
+                                         pro.b_stride);
+  // o must not alias any input; final_state may alias only the initial
+  // state (exactly: checked above)
+  if (in.hit(o, tok * 2) || in_no_h0.hit(final_state, st_bytes)) return KDA_ERR_INVALID_ARGUMENT;
   Ws ws;
   if ((st = carve(workspace, workspace_bytes, T, N, H, ws)) != KDA_OK) return st;
-  if (overlap(workspace, ws.L.total, o, tok * 2) ||
+  // the workspace is written while inputs are still being read
+  if (in.hit(workspace, ws.L.total) || overlap(workspace, ws.L.total, o, tok * 2) ||
       overlap(workspace, ws.L.total, final_state, st_bytes))
     return KDA_ERR_INVALID_ARGUMENT;
 
@@ -275,10 +320,16 @@ static kda_status decode_fwd_impl(const void *q, const void *k, const void *v, c
     return st;
   if ((st = check_outputs(initial_state, T, N, H, o, final_state)) != KDA_OK) return st;
   const int64_t tok = T * H * DK;
-  if (overlap(o, tok * 2, q, tok * 2) || overlap(o, tok * 2, k, tok * 2) ||
-      overlap(o, tok * 2, v, tok * 2) || overlap(o, tok * 2, g, tok * 4) ||
-      overlap(o, tok * 2, beta, T * H * 4) ||
-      (pro.b && overlap(o, tok * 2, pro.b, ((T - 1) * pro.b_stride + H) * 2)))
+  const int64_t st_bytes_all = (int64_t)N * H * DK * DV * 4;
+  const Inputs in = forward_inputs(q, k, v, g, beta, initial_state, cu_seqlens, T, N, H, pro.b,
+                                   pro.b_stride);
+  const Inputs in_no_h0 = forward_inputs(q, k, v, g, beta, nullptr, cu_seqlens, T, N, H, pro.b,
+                                         pro.b_stride);
+  // every workgroup reads cu_seqlens while others write o and the state
+  if (in.hit(o, tok * 2) || in_no_h0.hit(final_state, st_bytes_all))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (epi.y && T > 0 && (epi.z && overlap(final_state, st_bytes_all, epi.z,
+                                          ((T - 1) * epi.z_stride + (int64_t)H * DK) * 2)))
     return KDA_ERR_INVALID_ARGUMENT;
   if (epi.y && T > 0) {
     if (!epi.z || !epi.nw || !aligned(epi.y, 2) || !aligned(epi.z, 2) || !aligned(epi.nw, 4))

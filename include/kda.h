@@ -80,13 +80,18 @@ size_t kda_chunk_fwd_workspace_size(int64_t T, int32_t N, int32_t H);
  *                 T <= 2^31 - 1 and T * H * 128 must fit in int64
  *   scale         multiplies S^T q (1/sqrt(128) for the usual scaling)
  *   o             bf16 [T, H, 128] output, rounded to nearest even; must not
- *                 alias any input
+ *                 overlap any input (q, k, v, g, beta, cu_seqlens,
+ *                 initial_state)
  *   final_state   fp32 [N, H, 128, 128] output or NULL (not written); may
- *                 alias initial_state exactly (in-place update)
+ *                 alias initial_state exactly (in-place update) and must
+ *                 not overlap any other input
  *   workspace     256-byte aligned device scratch of workspace_bytes >=
  *                 kda_chunk_fwd_workspace_size(T, N, H); its contents on
- *                 entry do not matter and on return are unspecified; it
- *                 must not overlap o or final_state
+ *                 entry do not matter and on return are unspecified; it is
+ *                 written while the inputs are still being read, so it must
+ *                 not overlap o, final_state or any input
+ *   Overlaps that break these rules return KDA_ERR_INVALID_ARGUMENT before
+ *   anything is launched.
  *   stream        HIP stream the three kernels are enqueued on, in order
  *
  * A sequence's outputs depend only on its own tokens and initial state:
@@ -116,7 +121,13 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
  *
  * Arguments, layouts, aliasing and errors are those of kda_chunk_fwd
  * (initial_state NULL means zeros; final_state NULL is not written and may
- * alias initial_state exactly).  It needs no workspace and enqueues one
+ * alias initial_state exactly; o and final_state must not overlap any other
+ * input, cu_seqlens included, since every workgroup reads cu_seqlens while
+ * others write).  final_state NULL with T > 0 is the verification pass of
+ * speculative decoding: the window's outputs are formed and no state is
+ * kept; the accepted prefix is committed afterwards by a second call over
+ * the accepted tokens (cu_seqlens of the accepted lengths) from the same
+ * initial state.  It needs no workspace and enqueues one
  * kernel on `stream`.  KDA_ERR_UNSUPPORTED if N * H * 2 exceeds 2^31 - 1.
  */
 kda_status kda_decode_fwd(const void *q, const void *k, const void *v,

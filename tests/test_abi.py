@@ -90,6 +90,22 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert _fwd(lib, h0=8 << 20, hT=(8 << 20) + 256, ws_bytes=need) == INV
     # o overlapping the workspace
     assert _fwd(lib, o=(9 << 20) + 4096, ws_bytes=need) == INV
+    A = 1 << 20
+    # the workspace is written while every input is still being read: an
+    # overlap with any of them is rejected
+    for name in ("q", "k", "v", "g", "beta", "cu"):
+        assert _fwd(lib, ws=9 * A, ws_bytes=need, **{name: 9 * A + 4096}) == INV, name
+    assert _fwd(lib, ws=9 * A, ws_bytes=need, h0=9 * A + 8192) == INV
+    # o overlapping cu_seqlens or the initial state; final_state overlapping
+    # an input other than the initial state
+    assert _fwd(lib, ws_bytes=need, cu=7 * A + 256) == INV
+    assert _fwd(lib, ws_bytes=need, h0=7 * A + 4096) == INV
+    for name in ("q", "k", "v", "g", "beta", "cu"):
+        assert _fwd(lib, ws_bytes=need, **{name: 8 * A + 512}) == INV, name
+    # ... while final_state == initial_state (in place) is accepted by the
+    # host checks (a launch is never reached with these fake addresses only
+    # because the workspace check comes first in this call)
+    assert _fwd(lib, h0=8 * A, hT=8 * A) == 3
 
 
 def test_step_entry_points_reject_bad_arguments():
@@ -100,6 +116,15 @@ def test_step_entry_points_reject_bad_arguments():
     assert lib.kda_gate_cumsum(P, P, 10, 1, 1, 2 * P, 4 * P, 0, None) == 3
     assert lib.kda_gate_cumsum(P, P, 10, 1, 1, P, 4 * P, 10**9, None) == 1  # G aliases g
     assert lib.kda_chunk_intra(P, P, P, P, P, P, 10, 1, 1, 1.0, None, 10**9, None) == 1
+    # a workspace over an input of the intra step, or of the gate cumsum
+    W = 64 * P
+    assert lib.kda_chunk_intra(P, 2 * P, 3 * P, 4 * P, 5 * P, W + 512, 10, 1, 1, 1.0,
+                               W, 10**9, None) == 1
+    assert lib.kda_chunk_intra(W + 4096, 2 * P, 3 * P, 4 * P, 5 * P, 6 * P, 10, 1, 1, 1.0,
+                               W, 10**9, None) == 1
+    assert lib.kda_gate_cumsum(W + 4096, P, 10, 1, 1, 2 * P, W, 10**9, None) == 1
+    assert lib.kda_gate_cumsum(P, W + 256, 10, 1, 1, 2 * P, W, 10**9, None) == 1
+    assert lib.kda_gate_cumsum(P, 2 * P + 64, 10, 1, 1, 2 * P, W, 10**9, None) == 1  # G over cu
     out = (ctypes.c_int64 * 5)()
     assert lib.kda_workspace_layout(-5, 1, 1, out) == 1
 
@@ -124,6 +149,11 @@ def test_decode_entry_rejects_bad_arguments():
     assert dec(k=(2 << 20) + 8) == INV                     # misaligned
     assert dec(o=(3 << 20) + 64) == INV                    # o aliases v
     assert dec(h0=8 << 20, hT=(8 << 20) + 256) == INV     # partly overlapping states
+    # every workgroup reads cu_seqlens while others write o and the state
+    assert dec(cu=7 * A + 128) == INV                      # o over cu_seqlens
+    assert dec(h0=7 * A + 4096) == INV                     # o over the initial state
+    for name in ("q", "k", "v", "g", "beta", "cu"):
+        assert dec(**{name: 8 * A + 512}) == INV, name    # final_state over an input
 
 
 def test_fused_entries_reject_bad_arguments():
