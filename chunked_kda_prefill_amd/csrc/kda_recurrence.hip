@@ -58,10 +58,16 @@ __device__ __forceinline__ void dma_round(__amdgpu_buffer_rsrc_t r, uint32_t vof
   // the compiler cannot prove it
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base + off);
   const uint32_t soff = __builtin_amdgcn_readfirstlane(off);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
-               :
-               : "v"(voff), "s"(r), "s"(m0v), "s"(soff)
-               : "memory", "m0");
+  // M0 belongs to the compiler: its value is saved in a scratch SGPR and put
+  // back after the load has issued (the LDS address is taken from M0 at
+  // issue), so the asm hands every register back as it found it
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %4 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(r), "s"(m0v), "s"(soff)
+      : "memory");
 }
 // Buffer resource over one intermediate block, and the wave-uniform LDS
 // address of a block buffer.
