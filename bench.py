@@ -350,6 +350,22 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
+    # step-time distribution: a separate, untimed pass with events around
+    # every step (each event pair adds its own ~3.5 us to the interval)
+    dist_n = max(10, min(50, args.steps))
+    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(dist_n)]
+    for i, (ea, eb) in enumerate(dev_ev):
+        ea.record(stream)
+        step(sets[i % R])
+        eb.record(stream)
+    torch.cuda.synchronize()
+    dist = np.array([ea.elapsed_time(eb) * 1e3 for ea, eb in dev_ev])
+    step_dist = {"median": round(float(np.median(dist)), 2),
+                 "p10": round(float(np.percentile(dist, 10)), 2),
+                 "p90": round(float(np.percentile(dist, 90)), 2),
+                 "from": f"{dist_n} further steps, each bracketed by HIP events "
+                         "(not the timed region)"}
     ev = list(ev.values())
     intra_ms = [e[0].elapsed_time(e[1]) for e in ev]
     rec_ms = [e[1].elapsed_time(e[2]) for e in ev]
@@ -357,34 +373,45 @@ def main():
     rec_us = 1e3 * float(np.mean(rec_ms))
 
     # --- algorithmic bytes / flops ---------------------------------------
+    # Algorithmic bytes are what the operation must move: q, k, v, g, beta
+    # read, o written (1,540 B per (token, head)), plus the initial and final
+    # states.  The intermediate blocks the intra kernel writes and the
+    # recurrence reads back are this design's own traffic, not the
+    # operation's: they are reported separately (kernel_bytes_per_launch,
+    # traffic_rate), never in `achieved`.
     path_bytes = wl.algorithmic_bytes(w)
     path_flops = wl.algorithmic_flops(w)
     blocks = nc * H
     h0_bytes = 0 if w.initial_state is None else N * H * 128 * 128 * 4
-    # the intra kernel must read q, k, v, g, beta and write its blocks; the
-    # recurrence must read the blocks (+ initial state) and write o and the
-    # final state
     intra_bytes = T * H * (3 * 256 + 512 + 4) + blocks * BLOCK_BYTES
     rec_bytes = blocks * BLOCK_BYTES + h0_bytes + T * H * 256 + N * H * 128 * 128 * 4
     kern = {"kda_intra": (intra_us, intra_bytes), "kda_recurrence": (rec_us, rec_bytes)}
     dom = max(kern, key=lambda k: kern[k][0])
     dom_us, dom_bytes = kern[dom]
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    achieved = path_bytes / (dom_us * 1e-6) / 1e9
     step_s = elapsed / args.steps
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(w.name, dom),
+                "achieved_from": "the path's algorithmic bytes (q, k, v, g, beta, o, states) "
+                                 "per step / the dominant kernel's mean event time",
+                "path_frac": round(path_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
                 "kernel_us": {"kda_intra": round(intra_us, 2),
                               "kda_recurrence": round(rec_us, 2)},
                 "kernel_us_from": f"HIP events on {len(ev)} of the {args.steps} timed steps "
                                   f"(every {EVENT_STRIDE}th, from step {sampled[0]})",
                 "kernel_bytes_per_launch": {"kda_intra": intra_bytes,
-                                            "kda_recurrence": rec_bytes}}
+                                            "kda_recurrence": rec_bytes},
+                "traffic_rate": {k: round(b / (us * 1e-6) / 1e9, 1)
+                                 for k, (us, b) in kern.items()},
+                "traffic_rate_from": "kernel_bytes_per_launch (intermediate blocks included) "
+                                     "/ mean event time, GB/s"}
     path = {"algorithmic_bytes": path_bytes, "algorithmic_flops": path_flops,
             "GB/s": round(path_bytes / step_s / 1e9, 1),
             "hbm_frac": round(path_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
             "TFLOP/s": round(path_flops / step_s / 1e12, 2),
-            "mfma_frac": round(path_flops / step_s / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            "mfma_frac": round(path_flops / step_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "step_us": step_dist}
 
     # --- CPU baseline: the fp64 oracle on a bounded sample -----------------
     cpu = None

@@ -195,6 +195,13 @@ def long_single() -> Workload:
                          h0="normal", pinned_fraction=0.10)
 
 
+def e2e_4x32k() -> Workload:
+    """The end-to-end varlen shape of the KDA TPU report's correctness
+    section: four packed sequences of 32,768 tokens (512-chunk chains), here
+    at the headline's 16 heads with a cached-prefix state ~N(0, 0.1)."""
+    return make_workload("e2e_4x32768_H16", [32768] * 4, H=16, seed=4, h0="normal")
+
+
 def decode_step(users: int, tokens: int, H: int) -> Workload:
     """A decode step (tokens = 1) or a speculative-verification window
     (tokens = 4) for `users` sequences with cached states, ~N(0, 0.1)."""
@@ -236,6 +243,8 @@ def by_name(name: str) -> Workload:
         return sharegpt_like()
     if name == "long":
         return long_single()
+    if name == "e2e4x32k":
+        return e2e_4x32k()
     if name.startswith("decode"):  # decodeUxT_hH, e.g. decode16x1_h12
         ut, hh = name[len("decode"):].split("_h")
         u, t = ut.split("x")

@@ -96,6 +96,32 @@ def test_long_single_sequence(dev):
     parity(o[:, heads], f[:, heads], o_ref, f_ref, "long")
 
 
+def test_e2e_4x32k(dev):
+    # the KDA TPU report's end-to-end varlen shape (correctness section):
+    # 4 x 32,768 tokens, 512 chunks per chain, with a nonzero initial state
+    w = wl.e2e_4x32k()
+    heads = [2, 13]
+    log(f"[case] e2e 4x32768 H=16 (oracle on heads {heads})")
+    o, f = run_gpu(w, dev)
+    o_ref, f_ref = run_oracle(w, heads=heads)
+    parity(o[:, heads], f[:, heads], o_ref, f_ref, "e2e_4x32k")
+
+
+@pytest.mark.parametrize("gmul", [0.0, 0.01], ids=["g_zero", "weak_decay"])
+@pytest.mark.parametrize("shape", ["headline", "long"])
+def test_weak_and_no_decay_full_size(dev, shape, gmul):
+    # little or no decay at full length: the state carries the whole history
+    # (16,384 tokens in one chain for the long shape), at scale 1 where the
+    # max-abs bar bites; checked on sampled heads
+    w = wl.by_name(shape)
+    w.g = (w.g * np.float32(gmul)).astype(np.float32)
+    heads = [0, 47, 95] if shape == "long" else [0, 9]
+    log(f"[case] {shape} decay scaled by {gmul}, scale 1 (oracle on heads {heads})")
+    o, f = run_gpu(w, dev, scale=1.0)
+    o_ref, f_ref = run_oracle(w, scale=1.0, heads=heads)
+    parity(o[:, heads], f[:, heads], o_ref, f_ref, f"{shape} g*{gmul} scale 1")
+
+
 @pytest.mark.parametrize("N", [1024, 1100], ids=["N1024_table_in_intra", "N1100_table_kernel"])
 def test_many_sequences(dev, N):
     # up to 1024 sequences the intra-chunk kernel builds the chunk table
