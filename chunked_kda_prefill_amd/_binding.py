@@ -97,11 +97,10 @@ def workspace_size(T: int, N: int, H: int) -> int:
 
 
 def workspace_layout(T: int, N: int, H: int) -> dict:
-    out = (ctypes.c_int64 * 9)()
+    out = (ctypes.c_int64 * 5)()
     _check("kda_workspace_layout", load_library().kda_workspace_layout(T, N, H, out))
     return {"flags": out[0], "chunk_first": out[1], "chunk_info": out[2],
-            "blocks": out[3], "block_bytes": out[4], "sync": out[5], "order": out[6],
-            "units": out[7], "ready": out[8],
+            "blocks": out[3], "block_bytes": out[4],
             "nc_max": (T + (CHUNK - 1) * N) // CHUNK}
 
 

@@ -5,7 +5,6 @@
 #include "kda_chunk_table.h"
 #include "kda_internal.h"
 #include "kda_launch.h"
-#include "kda_plan.h"
 
 #include <stdint.h>
 
@@ -38,7 +37,6 @@ struct Ws {
   int32_t *flags;
   int32_t *chunk_first;
   int4 *chunk_info;
-  int32_t *sync, *order, *units, *ready;
   uint8_t *blocks;
 };
 
@@ -52,10 +50,6 @@ kda_status carve(void *workspace, size_t workspace_bytes, int64_t T, int32_t N, 
   ws.flags = reinterpret_cast<int32_t *>(base + ws.L.off_flags);
   ws.chunk_first = reinterpret_cast<int32_t *>(base + ws.L.off_chunk_first);
   ws.chunk_info = reinterpret_cast<int4 *>(base + ws.L.off_chunk_info);
-  ws.sync = reinterpret_cast<int32_t *>(base + ws.L.off_sync);
-  ws.order = reinterpret_cast<int32_t *>(base + ws.L.off_order);
-  ws.units = reinterpret_cast<int32_t *>(base + ws.L.off_units);
-  ws.ready = reinterpret_cast<int32_t *>(base + ws.L.off_ready);
   ws.blocks = base + ws.L.off_blocks;
   return KDA_OK;
 }
@@ -135,7 +129,7 @@ size_t kda_chunk_fwd_workspace_size(int64_t T, int32_t N, int32_t H) {
   return (size_t)ws_layout(T, N, H).total;
 }
 
-kda_status kda_workspace_layout(int64_t T, int32_t N, int32_t H, int64_t out[9]) {
+kda_status kda_workspace_layout(int64_t T, int32_t N, int32_t H, int64_t out[5]) {
   if (!out) return KDA_ERR_INVALID_ARGUMENT;
   const kda_status st = check_sizes(T, N, H);
   if (st != KDA_OK) return st;
@@ -145,10 +139,6 @@ kda_status kda_workspace_layout(int64_t T, int32_t N, int32_t H, int64_t out[9])
   out[2] = L.off_chunk_info;
   out[3] = L.off_blocks;
   out[4] = BLOCK_BYTES;
-  out[5] = L.off_sync;
-  out[6] = L.off_order;
-  out[7] = L.off_units;
-  out[8] = L.off_ready;
   return KDA_OK;
 }
 
@@ -227,77 +217,6 @@ struct Prologue {
   float qk_eps = -1.f;
 };
 
-static IntraArgs intra_args(const void *q, const void *k, const void *v, const float *g,
-                            const float *beta, const int32_t *cu_seqlens, int64_t T, int32_t N,
-                            int32_t H, float scale, const Ws &ws, bool inline_table,
-                            const Prologue &pro) {
-  IntraArgs ia;
-  ia.q = static_cast<const uint16_t *>(q);
-  ia.k = static_cast<const uint16_t *>(k);
-  ia.v = static_cast<const uint16_t *>(v);
-  ia.g = g;
-  ia.beta = beta;
-  ia.cu = cu_seqlens;
-  ia.chunk_first = ws.chunk_first;
-  ia.chunk_info = ws.chunk_info;
-  ia.flags = ws.flags;
-  ia.blocks = ws.blocks;
-  ia.nc_max = ws.L.nc_max;
-  ia.T = T;
-  ia.N = N;
-  ia.H = H;
-  ia.scale = scale;
-  ia.inline_table = inline_table ? 1 : 0;
-  ia.b = pro.b;
-  ia.b_stride = pro.b_stride;
-  ia.qk_eps = pro.qk_eps;
-  return ia;
-}
-
-// The single-launch path: the plan kernel, then intra-chunk producers and
-// chain consumers in one persistent grid (kda_plan.h).  Up to
-// PLAN_MAX_SEQS sequences.
-static kda_status run_single_launch(const void *q, const void *k, const void *v, const float *g,
-                                    const float *beta, const float *initial_state,
-                                    const int32_t *cu_seqlens, int64_t T, int32_t N, int32_t H,
-                                    float scale, void *o, float *final_state, const Ws &ws,
-                                    hipStream_t stream, const Prologue &pro) {
-  PlanArgs pa;
-  pa.cu = cu_seqlens;
-  pa.T = T;
-  pa.nc_max = ws.L.nc_max;
-  pa.N = N;
-  pa.H = H;
-  pa.chunk_first = ws.chunk_first;
-  pa.chunk_info = ws.chunk_info;
-  pa.flags = ws.flags;
-  pa.sync = ws.sync;
-  pa.order = ws.order;
-  pa.units = ws.units;
-  pa.ready = ws.ready;
-  if (launch_plan(pa, stream) != hipSuccess) return KDA_ERR_HIP;
-  FusedArgs fa;
-  fa.in = intra_args(q, k, v, g, beta, cu_seqlens, T, N, H, scale, ws, false, pro);
-  fa.co.blocks = ws.blocks;
-  fa.co.chunk_first = ws.chunk_first;
-  fa.co.chunk_info = ws.chunk_info;
-  fa.co.order = ws.order;
-  fa.co.ready = ws.ready;
-  fa.co.flags = ws.flags;
-  fa.co.diag = ws.sync + SYNC_DIAG;
-  fa.co.h0 = initial_state;
-  fa.co.hT = final_state;
-  fa.co.o = static_cast<uint16_t *>(o);
-  fa.co.nc_max = ws.L.nc_max;
-  fa.co.T = T;
-  fa.co.N = N;
-  fa.co.H = H;
-  fa.sync = ws.sync;
-  fa.units = ws.units;
-  fa.ready = ws.ready;
-  return hip_status(launch_fused(fa, stream));
-}
-
 static kda_status run_intra(const void *q, const void *k, const void *v, const float *g,
                             const float *beta, const int32_t *cu_seqlens, int64_t T, int32_t N,
                             int32_t H, float scale, const Ws &ws, hipStream_t stream,
@@ -374,9 +293,6 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
       overlap(workspace, ws.L.total, final_state, st_bytes))
     return KDA_ERR_INVALID_ARGUMENT;
 
-  if (N <= PLAN_MAX_SEQS)
-    return run_single_launch(q, k, v, g, beta, initial_state, cu_seqlens, T, N, H, scale, o,
-                             final_state, ws, stream, pro);
   if ((st = run_intra(q, k, v, g, beta, cu_seqlens, T, N, H, scale, ws, stream, pro)) != KDA_OK)
     return st;
   return run_recurrence(initial_state, T, N, H, o, final_state, ws, stream);

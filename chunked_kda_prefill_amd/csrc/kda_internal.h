@@ -96,26 +96,13 @@ __host__ __device__ constexpr int AQK_IDX(int mt, int s) {
   return (mt == 0 ? 0 : mt == 1 ? 1 : mt == 2 ? 2 : 4) + s;
 }
 
-// Workspace header: flags word, chunk_first[N+1], chunk_info[NCmax][4];
-// then what the single-launch path adds (kda_plan.h): its counters and the
-// per-XCD unit offsets (sync), the sequences sorted by chunk count (order),
-// the per-XCD chunk-major unit lists (units) and one ready flag per
-// intermediate block (ready); then the intermediate blocks.
+// Workspace header: flags word, chunk_first[N+1], chunk_info[NCmax][4].
 struct WsLayout {
-  int64_t off_flags, off_chunk_first, off_chunk_info, off_sync, off_order, off_units, off_ready,
-      off_blocks;
+  int64_t off_flags, off_chunk_first, off_chunk_info, off_blocks;
   int64_t nc_max, total;
 };
 
-// Bits of the workspace flags word.
-constexpr int FLAG_CLAMPED = 1;    // cu_seqlens was malformed and clamped
-constexpr int FLAG_TIMEOUT = 2;    // a bounded wait of the single-launch path gave up
-constexpr int FLAG_PLACEMENT = 4;  // a workgroup found no role on its XCD
-
 __host__ __device__ inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
-
-// bytes of the single launch's counters and offsets (kda_plan.h)
-constexpr int SYNC_BYTES = 4096;
 
 __host__ __device__ inline int64_t nc_max_of(int64_t T, int64_t N) {
   return (T + (int64_t)(BT - 1) * N) / BT;
@@ -127,12 +114,7 @@ __host__ __device__ inline WsLayout ws_layout(int64_t T, int64_t N, int64_t H) {
   L.off_flags = 0;
   L.off_chunk_first = 256;
   L.off_chunk_info = align256(L.off_chunk_first + 4 * (N + 1));
-  const int64_t units = H * (L.nc_max > 0 ? L.nc_max : 1);
-  L.off_sync = align256(L.off_chunk_info + 16 * (L.nc_max > 0 ? L.nc_max : 1));
-  L.off_order = L.off_sync + SYNC_BYTES;
-  L.off_units = align256(L.off_order + 4 * N);
-  L.off_ready = align256(L.off_units + 4 * units);
-  L.off_blocks = align256(L.off_ready + 4 * units);
+  L.off_blocks = align256(L.off_chunk_info + 16 * (L.nc_max > 0 ? L.nc_max : 1));
   L.total = L.off_blocks + H * L.nc_max * (int64_t)BLOCK_BYTES;
   return L;
 }

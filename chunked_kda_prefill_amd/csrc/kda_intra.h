@@ -4,8 +4,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "kda_consumer.h"
-
 namespace kda {
 
 struct IntraArgs {
@@ -32,18 +30,5 @@ struct IntraArgs {
   float qk_eps;
 };
 hipError_t launch_intra(const IntraArgs &a, hipStream_t stream);
-
-// The single-launch path (kda_plan.h, kda_consumer.h): `in` as for the
-// intra-chunk kernel (inline_table = 0: the plan kernel has written the
-// table), `co` for the chain consumers, and the plan's sync, unit lists and
-// ready flags.
-struct FusedArgs {
-  IntraArgs in;
-  ConsumerArgs co;
-  int32_t *sync;
-  const int32_t *units;
-  int32_t *ready;
-};
-hipError_t launch_fused(const FusedArgs &f, hipStream_t stream);
 
 }  // namespace kda

@@ -45,11 +45,9 @@
 // T_ab = -T_aa sum_{c=b}^{a-1} L_ac T_cb, needing only the other waves'
 // diagonal blocks.  All of it runs in fp32 on v_mfma_f32_16x16x4_f32.
 #include "kda_chunk_table.h"
-#include "kda_consumer.h"
 #include "kda_cumsum.h"
 #include "kda_internal.h"
 #include "kda_intra.h"
-#include "kda_plan.h"
 
 namespace kda {
 
@@ -187,9 +185,6 @@ constexpr int AUX_G = 0, AUX_QK = 0, AUX_V = CPOL_NT;
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-// s_waitcnt immediate: vector memory count 0, the other counters at their maxima
-constexpr int WAIT_VM0 = (0x7 << 4) | (0xF << 8);
-
 // Buffer over the unit's n valid rows (starting at row tb) of head h of a
 // [T, H, 128] tensor.  A lane whose row is past n addresses beyond the
 // record count, so the hardware range check returns zeros for it: rows past
@@ -285,33 +280,12 @@ __device__ __forceinline__ void load_v(const IntraArgs &a, int64_t t0, int n, in
     v[s] = __builtin_amdgcn_raw_buffer_load_b128(rv, 2 * (roff + 32 * s + 8 * load_m(grp)), 0, AUX_V);
 }
 
-// Producer state of the single-launch path: where the next unit comes from
-// and which block to flag ready.  Units are drawn from this XCD's list with
-// an atomic counter; the draw for the next unit is issued at the start of a
-// unit and its value read after the unit's second barrier.  The previous
-// unit's block is flagged ready at this unit's first barrier: by then every
-// wave has waited for its block stores (they sit in this XCD's L2), and the
-// only vector memory operations since were loads already consumed.  The
-// flag is a relaxed device-scope atomic store (cache policy sc1).
-struct FusedCtl {
-  int32_t *grab;         // this XCD's unit counter
-  const int32_t *list;   // this XCD's units, chunk-major (c * H + h)
-  int32_t units;         // entries in the list
-  int32_t *ready;        // block ready flags [H * nc_max]
-  int64_t prev_block;    // block of the previous unit, not yet flagged (-1: none)
-  int32_t *slot;         // LDS word for the drawn index
-};
-
 // One (chunk, head) unit whose inputs are already in `nxt` (loads issued).
 // After the unit's own inputs are consumed, `nxt` receives the next unit's.
-// Static schedule (FUSED = false): the next unit is (cn, hn) if `more`.
-// Single launch (FUSED = true): the next unit is drawn from ctl's list, and
-// more, cn and hn are set to it.
-template <bool NORM, bool FUSED>
+template <bool NORM>
 __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, int c, int h,
-                                           bool &more, int &cn, int &hn, UnitInputs &nxt,
-                                           const int32_t *first_lds, int &s_next,
-                                           FusedCtl *ctl = nullptr) {
+                                           bool more, int cn, int hn, UnitInputs &nxt,
+                                           const int32_t *first_lds, int &s_next) {
   // threadIdx.x through an opaque move, so that address arithmetic derived
   // from it stays inside the unit loop instead of being hoisted out of it
   int tid;
@@ -323,15 +297,8 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   const int l = tid & 63, nn = l & 15, grp = l >> 4;
   const int row = SB * w + nn;
   // the next unit's chunk record, fetched now so that its data loads can be
-  // issued later without waiting on it (single launch: once it is drawn)
-  int4 info_next;
-  int32_t drawn = 0;
-  if constexpr (!FUSED) {
-    info_next = unit_record(a, first_lds, more ? cn : c, s_next);
-  } else {
-    // the draw's latency hides behind the cumsum and table phases
-    if (tid == 0) drawn = atomicAdd(ctl->grab, 1);
-  }
+  // issued later without waiting on it
+  const int4 info_next = unit_record(a, first_lds, more ? cn : c, s_next);
   // The unit's inputs are read in place: each part of `nxt` is consumed
   // before the next unit's loads into that part are issued (g and beta in
   // the cumsum phase, q and k in the factor phase), so no register copy of
@@ -360,17 +327,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
       *reinterpret_cast<float4 *>(&rt[(4 + w) * DK + slot_ch(j, grp)]) = G[j];
   }
   if (grp == 0) sm.beta[row] = a.b ? (row < n ? 1.f / (1.f + expf(-in.beta)) : 0.f) : in.beta;
-  if constexpr (FUSED) {
-    // the previous unit's block stores are complete (in L2) in every wave
-    // once all of them pass this barrier
-    if (ctl->prev_block >= 0) __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-  }
   __syncthreads();
-  if constexpr (FUSED) {
-    if (ctl->prev_block >= 0 && tid == 0)
-      __hip_atomic_store(ctl->ready + ctl->prev_block, 1, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  }
 
   // ---- per-channel tables (two threads per channel) ----
   {
@@ -393,23 +350,8 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
       sm.tab[TAB_GAM][ch] = exp_nat(acc);
     }
   }
-  if constexpr (FUSED) {
-    if (tid == 0) *ctl->slot = drawn;
-  }
 
   __syncthreads();
-  if constexpr (FUSED) {
-    // the unit drawn at the start: this XCD's list entry c * H + h
-    const int32_t k = *ctl->slot;
-    more = k < ctl->units;
-    if (more) {
-      const int32_t un =
-          ((const __attribute__((address_space(4))) int32_t *)(uintptr_t)ctl->list)[k];
-      cn = un / a.H;
-      hn = un - cn * a.H;
-      info_next = chunk_record(a.chunk_info, cn);
-    }
-  }
 
   // ---- per-element factors for the wave's own rows, straight into operand
   // fragments; q*Gamma fragments (token tile w); K*Gamma and kg rows for
@@ -889,109 +831,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void in
       hn -= a.H;
       ++cn;
     }
-    bool more_ = more;
-    intra_unit<NORM, false>(a, sm, c, h, more_, cn, hn, nxt, first_lds, s_next);
+    intra_unit<NORM>(a, sm, c, h, more, cn, hn, nxt, first_lds, s_next);
     if (!more) break;
     u += G;
     c = cn;
     h = hn;
   }
-}
-
-// ---------------------------------------------------------------------------
-// Single launch (kda_plan.h): intra-chunk producers and chain consumers in
-// one persistent grid of two workgroups per CU.  A workgroup reads the XCD
-// it runs on and draws a ticket there; the first min(chains of the XCD,
-// MAX_CONSUMERS) tickets consume that XCD's chains (ranks rho = xcd + 8 i,
-// ticket t taking i = t, t + consumers, ...), the rest produce its units in
-// the plan's chunk-major order.  Producers never wait; a consumer waits
-// (bounded) only for blocks of its chain that producers of its XCD have
-// drawn or will draw, so the grid makes progress whenever each XCD has one
-// producer resident beside its consumers.
-// ---------------------------------------------------------------------------
-template <bool NORM>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void fused_kernel(
-    FusedArgs f) {
-  __shared__ IntraSmem sm;
-  __shared__ int32_t slot[2];
-  const IntraArgs &a = f.in;
-  const int tid = threadIdx.x;
-  uint32_t xcc_raw;
-  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc_raw));
-  const int xcc = (int)(xcc_raw & 0xF);
-  if (xcc >= XCDS) {
-    if (tid == 0) atomicOr(a.flags, FLAG_PLACEMENT);
-    return;
-  }
-  if (tid == 0) slot[0] = atomicAdd(f.sync + SYNC_TICKET + SYNC_STRIDE * xcc, 1);
-  __syncthreads();
-  const int ticket = __builtin_amdgcn_readfirstlane(slot[0]);
-  const int64_t chains = (int64_t)a.N * a.H;
-  const int64_t chains_x = chains > xcc ? (chains - xcc + XCDS - 1) / XCDS : 0;
-  const int consumers = (int)(chains_x < MAX_CONSUMERS ? chains_x : MAX_CONSUMERS);
-  // the wave index in a scalar register: role branches are scalar jumps
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l = tid & 63;
-
-  if (ticket < consumers) {
-    // the chain's latency bounds the call: its waves are issued first
-    __builtin_amdgcn_s_setprio(3);
-    bool gave_up = false;
-    for (int64_t rho = xcc + (int64_t)XCDS * ticket; rho < chains;
-         rho += (int64_t)XCDS * consumers) {
-      const int i = (int)(rho / a.H), h = (int)(rho - (int64_t)i * a.H);
-      const int sq = ((const __attribute__((address_space(4))) int32_t *)(uintptr_t)f.co.order)[i];
-      consume_chain(f.co, reinterpret_cast<uint8_t *>(&sm), sq, h, w, l, gave_up);
-    }
-    return;
-  }
-
-  __builtin_amdgcn_s_setprio(1);
-  FusedCtl ctl;
-  const int32_t xoff = f.sync[SYNC_XOFF + xcc], xend = f.sync[SYNC_XOFF + xcc + 1];
-  ctl.grab = f.sync + SYNC_UNIT + SYNC_STRIDE * xcc;
-  ctl.list = f.units + xoff;
-  ctl.units = xend - xoff;
-  ctl.ready = f.ready;
-  ctl.prev_block = -1;
-  ctl.slot = &slot[1];
-  if (tid == 0) slot[1] = atomicAdd(ctl.grab, 1);
-  __syncthreads();
-  const int32_t k0 = slot[1];
-  if (k0 >= ctl.units) return;
-  const int32_t u0 = ((const __attribute__((address_space(4))) int32_t *)(uintptr_t)ctl.list)[k0];
-  int c = u0 / a.H, h = u0 - (u0 / a.H) * a.H;
-  UnitInputs nxt;
-  load_unit(a, chunk_record(a.chunk_info, c), h, SB * (tid >> 6) + (tid & 15), (tid >> 4) & 3, nxt);
-  int s_unused = 0;
-  for (;;) {
-    bool more = false;
-    int cn = 0, hn = 0;
-    intra_unit<NORM, true>(a, sm, c, h, more, cn, hn, nxt, nullptr, s_unused, &ctl);
-    ctl.prev_block = (int64_t)h * a.nc_max + c;
-    if (!more) break;
-    c = cn;
-    h = hn;
-  }
-  // the last unit's block: every wave's stores complete, then the flag
-  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
-  __syncthreads();
-  if (tid == 0)
-    __hip_atomic_store(ctl.ready + ctl.prev_block, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-hipError_t launch_fused(const FusedArgs &f, hipStream_t stream) {
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  const int grid = 2 * cus;  // two workgroups per CU, all resident at once
-  if (grid < XCDS * (MAX_CONSUMERS + 1)) return hipErrorInvalidConfiguration;
-  if (f.in.qk_eps >= 0.f)
-    hipLaunchKernelGGL(fused_kernel<true>, dim3((unsigned)grid), dim3(NT), 0, stream, f);
-  else
-    hipLaunchKernelGGL(fused_kernel<false>, dim3((unsigned)grid), dim3(NT), 0, stream, f);
-  return hipGetLastError();
 }
 
 hipError_t launch_intra(const IntraArgs &a, hipStream_t stream) {

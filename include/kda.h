@@ -310,15 +310,13 @@ kda_status kda_chunk_recurrence(const float *initial_state, int64_t T, int32_t N
 
 /*
  * Where things live inside the workspace, for the step-level tests.
- * kda_workspace_layout fills out[0..8] = byte offsets of (flags,
- * chunk_first, chunk_info, first intermediate block), the block size in
- * bytes, then the byte offsets of the single launch's regions (sync: per-XCD
- * counters and unit-list offsets; order: the sequences sorted by chunk
- * count; units: the per-XCD unit lists; ready: one flag per block).  The
- * block of (head h, chunk c) starts at out[3] + (h * NCmax + c) * out[4].
- * Returns KDA_ERR_INVALID_ARGUMENT for bad sizes.
+ * kda_workspace_layout fills out[0..4] = byte offsets of (flags,
+ * chunk_first, chunk_info, first intermediate block) and the block size
+ * in bytes; the block of (head h, chunk c) starts at
+ * out[3] + (h * NCmax + c) * out[4].  Returns KDA_ERR_INVALID_ARGUMENT for
+ * bad sizes.
  */
-kda_status kda_workspace_layout(int64_t T, int32_t N, int32_t H, int64_t out[9]);
+kda_status kda_workspace_layout(int64_t T, int32_t N, int32_t H, int64_t out[5]);
 
 #ifdef __cplusplus
 }

@@ -45,13 +45,7 @@ def test_workspace_size_and_layout():
     for key in ("chunk_first", "chunk_info", "blocks"):
         assert lay[key] % 256 == 0
     assert lay["chunk_info"] >= lay["chunk_first"] + 4 * (N + 1)
-    assert lay["sync"] >= lay["chunk_info"] + 16 * lay["nc_max"]
-    assert lay["order"] >= lay["sync"] + 4 * 288            # counters and list offsets
-    assert lay["units"] >= lay["order"] + 4 * N
-    assert lay["ready"] >= lay["units"] + 4 * H * lay["nc_max"]
-    assert lay["blocks"] >= lay["ready"] + 4 * H * lay["nc_max"]
-    for key in ("sync", "order", "units", "ready"):
-        assert lay[key] % 256 == 0
+    assert lay["blocks"] >= lay["chunk_info"] + 16 * lay["nc_max"]
     assert kda.workspace_size(T, N, H) == lay["blocks"] + H * lay["nc_max"] * 72192
     assert kda.workspace_size(0, 1, 1) > 0
     for bad in [(-1, 1, 1), (10, 0, 1), (10, 1, 0)]:
@@ -131,7 +125,7 @@ def test_step_entry_points_reject_bad_arguments():
     assert lib.kda_gate_cumsum(W + 4096, P, 10, 1, 1, 2 * P, W, 10**9, None) == 1
     assert lib.kda_gate_cumsum(P, W + 256, 10, 1, 1, 2 * P, W, 10**9, None) == 1
     assert lib.kda_gate_cumsum(P, 2 * P + 64, 10, 1, 1, 2 * P, W, 10**9, None) == 1  # G over cu
-    out = (ctypes.c_int64 * 9)()
+    out = (ctypes.c_int64 * 5)()
     assert lib.kda_workspace_layout(-5, 1, 1, out) == 1
 
 

@@ -11,12 +11,11 @@
    branch, loops iterated to a fixpoint); a saveexec narrows it, and an
    explicit restore of EXEC (s_or_b64 / s_mov_b64 into exec) ends it.
 
-2. The LDS-DMA inline assembly (the recurrence kernel and the single
-   launch's chain consumer) writes M0, which the compiler owns: it saves M0
-   to a scratch SGPR first and restores it after the load has issued.  The
-   guard checks that every write of M0 in those kernels is one of those
-   save / set / restore sequences around a buffer_load ... lds, so no value
-   of the compiler's is ever lost."""
+2. The recurrence's LDS-DMA inline assembly writes M0, which the compiler
+   owns: it saves M0 to a scratch SGPR first and restores it after the load
+   has issued.  The guard checks that every write of M0 in the recurrence
+   kernels is one of those save / set / restore sequences around a
+   buffer_load ... lds, so no value of the compiler's is ever lost."""
 
 import os
 import re
@@ -221,11 +220,8 @@ def test_m0_scanner():
 
 
 @pytest.mark.skipif(shutil.which("hipcc") is None, reason="hipcc not available")
-@pytest.mark.parametrize("src", ["kda_recurrence.hip", "kda_intra.hip"])
-def test_lds_dma_preserves_m0(src, tmp_path):
-    # the recurrence kernel and the single launch's chain consumer (compiled
-    # with the intra-chunk kernel) both copy blocks with LDS DMA
-    asm, err = _compile(src, tmp_path)
+def test_recurrence_m0_is_preserved(tmp_path):
+    asm, err = _compile("kda_recurrence.hip", tmp_path)
     assert "clobber list contains reserved registers" not in err
     assert "lds" in asm
     bad = m0_writes_outside_dma(asm)

@@ -190,41 +190,3 @@ def test_intra_intermediates(dev, lens, scale):
     # Aqk: bf16 strip operands (one rounding each side), then bf16 storage
     assert worst["Aqk"] < 8e-3
     assert worst["gamma"] < 1e-4
-
-
-@pytest.mark.parametrize("lens,H", [([2048] * 4, 16), ([130, 0, 64, 17, 200, 1, 0, 95], 3),
-                                    ([700, 5, 3000, 64, 65, 1, 128], 5)],
-                         ids=["headline_shape", "varlen_empty", "mixed"])
-def test_single_launch_plan_tables(dev, lens, H):
-    # what the plan kernel leaves in the workspace for the single launch: the
-    # sequences sorted by chunk count, the per-XCD chunk-major unit lists and
-    # their offsets, against the construction pinned on the CPU
-    # (test_protocol_model.plan_lists); after the call every block's ready
-    # flag is set, every XCD's units were all drawn, and no wait timed out
-    import torch
-    import chunked_kda_prefill_amd as kda
-    from test_protocol_model import plan_lists
-    w = wl.make_workload("plan_tables", lens, H=H, seed=36)
-    log(f"[plan] lens={lens} H={H}")
-    t = wl.to_torch(w, dev)
-    ws = kda.new_workspace(w.T, w.N, w.H, dev).fill_(0x5A)
-    kda.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"],
-                  initial_state=t["initial_state"], scale=w.scale, workspace=ws)
-    torch.cuda.synchronize()
-    lay = kda.workspace_layout(w.T, w.N, w.H)
-    raw = ws.cpu().numpy()
-    i32 = lambda off, n: raw[off:off + 4 * n].view(np.int32)
-    assert int(i32(lay["flags"], 1)[0]) == 0
-    order, first, lists = plan_lists(lens, H)
-    assert list(i32(lay["order"], w.N)) == order
-    sync = i32(lay["sync"], 288)
-    xoff = list(sync[256:265])
-    assert xoff == list(np.concatenate([[0], np.cumsum([len(x) for x in lists])]))
-    units = i32(lay["units"], xoff[-1])
-    for x in range(8):
-        got = [(int(u) // H, int(u) % H) for u in units[xoff[x]:xoff[x + 1]]]
-        assert got == lists[x], x
-        assert int(sync[32 * x + 1]) >= len(lists[x])      # every unit was drawn
-    ready = i32(lay["ready"], H * lay["nc_max"]).reshape(H, lay["nc_max"])
-    nc = first[-1]
-    assert np.all(ready[:, :nc] == 1)
