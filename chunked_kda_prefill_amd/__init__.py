@@ -9,8 +9,10 @@ from ._binding import (  # noqa: F401
     EXPORTED,
     KDAError,
     LIB_PATH,
+    NOALLOC_WORKSPACE_BYTES,
     chunk_fwd,
     chunk_fwd_fused,
+    chunk_fwd_noalloc,
     chunk_intra,
     chunk_recurrence,
     chunk_table,

@@ -27,7 +27,7 @@ EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd"
             "kda_chunk_table", "kda_gate_cumsum", "kda_chunk_intra",
             "kda_workspace_layout", "kda_chunk_recurrence", "kda_decode_fwd",
             "kda_chunk_fwd_fused", "kda_decode_fwd_fused", "kda_gated_rmsnorm",
-            "kda_decode_step_fused", "kda_validate_inputs")
+            "kda_decode_step_fused", "kda_validate_inputs", "kda_chunk_fwd_noalloc")
 VALIDATION_BITS = {1: "cu_seqlens", 2: "g", 4: "beta"}
 ACTIVATIONS = {"sigmoid": 0, "silu": 1}
 
@@ -59,6 +59,8 @@ def load_library():
     lib.kda_chunk_fwd_workspace_size.restype = SZ
     lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F32, P, P, P, SZ, P]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F32, P, P, P]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_decode_fwd.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F32, P, P, P]
     lib.kda_decode_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd_fused.argtypes = [P, P, P, P, P, I64, F32, P, P, I64, I32, I32, F32, P, P, P,
@@ -194,6 +196,31 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, scale: Optional[
         T, N, H, float(scale), _ptr(o), _ptr(final_state), _ptr(workspace),
         workspace.numel(), _stream(dev))
     _check("kda_chunk_fwd", st)
+    return o, final_state
+
+
+NOALLOC_WORKSPACE_BYTES = 160 << 20
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, cu_seqlens, o, final_state=None, initial_state=None,
+                      scale: Optional[float] = None):
+    """kda_chunk_fwd_noalloc: the chunked forward with the library's own
+    per-GPU workspace.  The caller passes the outputs (o bf16 [T, H, 128],
+    final_state fp32 [N, H, 128, 128] or None); nothing is allocated.
+    Calls that overlap in time on one GPU race."""
+    torch = _torch()
+    T, N, H = _check_inputs(q, k, v, g, beta, cu_seqlens)
+    if initial_state is not None:
+        _expect(initial_state, "initial_state", torch.float32, (N, H, HEAD_DIM, HEAD_DIM))
+    _expect(o, "o", torch.bfloat16, (T, H, HEAD_DIM))
+    if final_state is not None:
+        _expect(final_state, "final_state", torch.float32, (N, H, HEAD_DIM, HEAD_DIM))
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    st = load_library().kda_chunk_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+        T, N, H, float(scale), _ptr(o), _ptr(final_state), _stream(q.device))
+    _check("kda_chunk_fwd_noalloc", st)
     return o, final_state
 
 

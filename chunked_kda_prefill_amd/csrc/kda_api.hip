@@ -6,9 +6,46 @@
 #include "kda_internal.h"
 #include "kda_launch.h"
 
+#include <mutex>
 #include <stdint.h>
 
 using namespace kda;
+
+// ---------------------------------------------------------------------------
+// Workspace of kda_chunk_fwd_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not the device memory: its device address is looked up
+// once per device (hipGetSymbolAddress, with that device current) and only
+// that address is handed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[KDA_NOALLOC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::once_flag scratch_once[MAX_DEVICES];
+void *scratch_ptr[MAX_DEVICES];
+hipError_t scratch_err[MAX_DEVICES];
+
+// The calling thread's current device's copy of `scratch`, or null (with
+// the lookup's error in *err).
+void *device_scratch(hipError_t *err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(scratch_once[dev], [dev]() {
+    void *p = nullptr;
+    scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    scratch_ptr[dev] = scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *err = scratch_err[dev];
+  return scratch_ptr[dev];
+}
+
+}  // namespace
 
 namespace {
 
@@ -267,11 +304,14 @@ kda_status kda_chunk_intra(const void *q, const void *k, const void *v, const fl
   return run_intra(q, k, v, g, beta, cu_seqlens, T, N, H, scale, ws, stream);
 }
 
-static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const float *g,
-                                 const float *beta, const float *initial_state,
-                                 const int32_t *cu_seqlens, int64_t T, int32_t N, int32_t H,
-                                 float scale, void *o, float *final_state, void *workspace,
-                                 size_t workspace_bytes, hipStream_t stream, const Prologue &pro) {
+// Host-side checks of a forward call's arguments (sizes, pointers, alignment,
+// overlaps): o must not overlap any input; final_state may alias only the
+// initial state, exactly.
+static kda_status check_forward_args(const void *q, const void *k, const void *v, const float *g,
+                                     const float *beta, const float *initial_state,
+                                     const int32_t *cu_seqlens, int64_t T, int32_t N, int32_t H,
+                                     const void *o, const float *final_state,
+                                     const Prologue &pro) {
   kda_status st = check_sizes(T, N, H);
   if (st != KDA_OK) return st;
   if ((st = check_inputs(q, k, v, g, beta, cu_seqlens, T, pro.b, pro.b_stride, H)) != KDA_OK)
@@ -283,9 +323,22 @@ static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, co
                                    pro.b_stride);
   const Inputs in_no_h0 = forward_inputs(q, k, v, g, beta, nullptr, cu_seqlens, T, N, H, pro.b,
                                          pro.b_stride);
-  // o must not alias any input; final_state may alias only the initial
-  // state (exactly: checked above)
   if (in.hit(o, tok * 2) || in_no_h0.hit(final_state, st_bytes)) return KDA_ERR_INVALID_ARGUMENT;
+  return KDA_OK;
+}
+
+static kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *initial_state,
+                                 const int32_t *cu_seqlens, int64_t T, int32_t N, int32_t H,
+                                 float scale, void *o, float *final_state, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream, const Prologue &pro) {
+  kda_status st = check_forward_args(q, k, v, g, beta, initial_state, cu_seqlens, T, N, H, o,
+                                     final_state, pro);
+  if (st != KDA_OK) return st;
+  const int64_t tok = T * H * DK;
+  const int64_t st_bytes = (int64_t)N * H * DK * DV * 4;
+  const Inputs in = forward_inputs(q, k, v, g, beta, initial_state, cu_seqlens, T, N, H, pro.b,
+                                   pro.b_stride);
   Ws ws;
   if ((st = carve(workspace, workspace_bytes, T, N, H, ws)) != KDA_OK) return st;
   // the workspace is written while inputs are still being read
@@ -400,6 +453,25 @@ kda_status kda_chunk_fwd_fused(const void *q, const void *k, const void *v, cons
   pro.qk_eps = qk_eps >= 0.f ? qk_eps : -1.f;
   return chunk_fwd_impl(q, k, v, g, nullptr, initial_state, cu_seqlens, T, N, H, scale, o,
                         final_state, workspace, workspace_bytes, stream, pro);
+}
+
+kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *initial_state,
+                                 const int32_t *cu_seqlens, int64_t T, int32_t N, int32_t H,
+                                 float scale, void *o, float *final_state, hipStream_t stream) {
+  kda_status st = check_sizes(T, N, H);
+  if (st != KDA_OK) return st;
+  const int64_t need = ws_layout(T, N, H).total;
+  if (need > (int64_t)KDA_NOALLOC_WORKSPACE_BYTES) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  // host-side argument checks first: nothing touches the device before them
+  if ((st = check_forward_args(q, k, v, g, beta, initial_state, cu_seqlens, T, N, H, o,
+                               final_state, Prologue())) != KDA_OK)
+    return st;
+  hipError_t e = hipSuccess;
+  void *ws = device_scratch(&e);
+  if (!ws) return KDA_ERR_HIP;
+  return chunk_fwd_impl(q, k, v, g, beta, initial_state, cu_seqlens, T, N, H, scale, o,
+                        final_state, ws, KDA_NOALLOC_WORKSPACE_BYTES, stream, Prologue());
 }
 
 kda_status kda_decode_fwd(const void *q, const void *k, const void *v, const float *g,

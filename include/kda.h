@@ -107,6 +107,33 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
                          hipStream_t stream);
 
 /*
+ * kda_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The workspace is a file-scope device
+ * array of KDA_NOALLOC_WORKSPACE_BYTES inside the library, one per GPU,
+ * allocated when the library's code is loaded on that GPU and held until the
+ * process ends; its address is looked up on the first call on each device.
+ * The call itself allocates nothing.
+ *
+ * Arguments, results and errors are those of kda_chunk_fwd.  Sizes whose
+ * workspace (kda_chunk_fwd_workspace_size) exceeds the array return
+ * KDA_ERR_WORKSPACE_TOO_SMALL before any launch; the headline shape of 4 x
+ * 2048 tokens at 16 heads needs 144.3 MiB of it.  KDA_ERR_HIP if the array's
+ * address cannot be obtained on the current device.
+ *
+ * Every call on a GPU uses that GPU's one array: calls that overlap in time
+ * on one GPU (other streams, other threads) race and must not be issued;
+ * calls in stream order on one stream are safe.  The array keeps the last
+ * call's contents, which no call depends on.
+ */
+#define KDA_NOALLOC_WORKSPACE_BYTES ((size_t)160 << 20)
+kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta,
+                                 const float *initial_state, const int32_t *cu_seqlens,
+                                 int64_t T, int32_t N, int32_t H, float scale,
+                                 void *o, float *final_state, hipStream_t stream);
+
+/*
  * Token-serial KDA forward for decode and speculative verification (MI355X
  * Kimi K3 post, sections 1.2-1.3: one fused kernel applies each sequence's
  * new tokens, 1 for a decode step or a window of a few for verification,

@@ -258,3 +258,26 @@ def test_python_wrapper_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _binding.load_library()
+
+
+def test_noalloc_entry_checks_before_any_device_call():
+    # kda_chunk_fwd_noalloc rejects sizes whose workspace exceeds its
+    # library-owned array, and bad arguments, before it looks at any device
+    lib = kda.load_library()
+    A = 1 << 20
+
+    def call(**over):
+        a = dict(q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, h0=None, cu=6 * A, T=128, N=1,
+                 H=2, scale=1.0, o=7 * A, hT=8 * A)
+        a.update(over)
+        return lib.kda_chunk_fwd_noalloc(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"],
+                                         a["cu"], a["T"], a["N"], a["H"], a["scale"], a["o"],
+                                         a["hT"], None)
+    INV, WS = 1, 3
+    limit = kda.NOALLOC_WORKSPACE_BYTES
+    assert kda.workspace_size(8192, 4, 16) <= limit          # the headline shape fits
+    assert kda.workspace_size(16384, 1, 96) > limit          # the long shape does not
+    assert call(T=16384, N=1, H=96) == WS
+    assert call(q=None) == INV
+    assert call(T=-1) == INV
+    assert call(o=(1 << 20) + 64) == INV                      # o over q
