@@ -90,6 +90,9 @@ SWEEP_CONFIGS = ["tiny", "headline"] + [f"batch{b}" for b in (1, 2, 4, 8, 16, 32
 # configs also timed through the fused-prologue entry points, and with the
 # same prologue done by separate torch ops in front of the plain entry point
 FUSED_SWEEP_CONFIGS = ("headline", "long", "decode16x1_h12", "decode16x4_h12", "decode64x1_h96")
+# configs also timed with chunk-parallel state passing (kda_chunk_fwd_segmented)
+# at these segment counts: the A/B of few, long chains
+SEGMENT_SWEEP = {"batch1": (4, 8), "batch2": (4, 8), "long": (2, 4)}
 
 
 def sweep(args, torch, np, kda, wl):
@@ -142,6 +145,7 @@ def sweep(args, torch, np, kda, wl):
             main = main + [e + "_fused" for e in main] + ["torch prologue + " + main[0]]
             if n.startswith("decode"):
                 main += ["decode_step_fused", "norm after decode_fwd_fused"]
+        main += [f"segmented {p}" for p in SEGMENT_SWEEP.get(n, ())]
         runs += [(n, e) for e in main]
     for name, entry in runs:
         w = wl.by_name(name)
@@ -166,7 +170,15 @@ def sweep(args, torch, np, kda, wl):
         is_dec = entry.split(" + ")[-1].startswith("decode_fwd")
         plain = kda.decode_fwd if is_dec else kda.chunk_fwd
         extra = {} if is_dec else {"workspace": ws}
-        if entry == "decode_step_fused":
+        if entry.startswith("segmented"):
+            nseg = int(entry.split()[1])
+            sws = torch.empty(kda.load_library().kda_chunk_fwd_segmented_workspace_size(
+                T, N, H, nseg), dtype=torch.uint8, device=dev)
+            call = lambda: kda.chunk_fwd_segmented(
+                t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu_seqlens"], nseg,
+                initial_state=t["initial_state"], scale=w.scale, o=o, final_state=fin,
+                workspace=sws)
+        elif entry == "decode_step_fused":
             call = lambda: kda.decode_step_fused(
                 t["q"], t["k"], t["v"], t["g"], blog, t["cu_seqlens"], z, nwt,
                 initial_state=t["initial_state"], scale=w.scale, o=o, y=ybuf, final_state=fin)

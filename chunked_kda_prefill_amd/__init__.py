@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     chunk_fwd,
     chunk_fwd_fused,
     chunk_fwd_noalloc,
+    chunk_fwd_segmented,
     chunk_intra,
     chunk_recurrence,
     chunk_table,

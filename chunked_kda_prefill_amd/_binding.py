@@ -27,7 +27,8 @@ EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd"
             "kda_chunk_table", "kda_gate_cumsum", "kda_chunk_intra",
             "kda_workspace_layout", "kda_chunk_recurrence", "kda_decode_fwd",
             "kda_chunk_fwd_fused", "kda_decode_fwd_fused", "kda_gated_rmsnorm",
-            "kda_decode_step_fused", "kda_validate_inputs", "kda_chunk_fwd_noalloc")
+            "kda_decode_step_fused", "kda_validate_inputs", "kda_chunk_fwd_noalloc",
+            "kda_chunk_fwd_segmented", "kda_chunk_fwd_segmented_workspace_size")
 VALIDATION_BITS = {1: "cu_seqlens", 2: "g", 4: "beta"}
 ACTIVATIONS = {"sigmoid": 0, "silu": 1}
 
@@ -59,6 +60,11 @@ def load_library():
     lib.kda_chunk_fwd_workspace_size.restype = SZ
     lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F32, P, P, P, SZ, P]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_segmented.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F32, I32, P, P,
+                                            P, SZ, P]
+    lib.kda_chunk_fwd_segmented.restype = ctypes.c_int
+    lib.kda_chunk_fwd_segmented_workspace_size.argtypes = [I64, I32, I32, I32]
+    lib.kda_chunk_fwd_segmented_workspace_size.restype = SZ
     lib.kda_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F32, P, P, P]
     lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_decode_fwd.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, F32, P, P, P]
@@ -196,6 +202,40 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, initial_state=None, scale: Optional[
         T, N, H, float(scale), _ptr(o), _ptr(final_state), _ptr(workspace),
         workspace.numel(), _stream(dev))
     _check("kda_chunk_fwd", st)
+    return o, final_state
+
+
+def chunk_fwd_segmented(q, k, v, g, beta, cu_seqlens, segments: int, initial_state=None,
+                        scale: Optional[float] = None, output_final_state: bool = True,
+                        workspace=None, o=None, final_state=None):
+    """kda_chunk_fwd_segmented: the chunked forward with chunk-parallel state
+    passing, each chain cut into `segments` runs.  Returns (o, final_state)."""
+    torch = _torch()
+    T, N, H = _check_inputs(q, k, v, g, beta, cu_seqlens)
+    dev = q.device
+    if initial_state is not None:
+        _expect(initial_state, "initial_state", torch.float32, (N, H, HEAD_DIM, HEAD_DIM))
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    if o is None:
+        o = torch.empty((T, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    else:
+        _expect(o, "o", torch.bfloat16, (T, H, HEAD_DIM))
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, HEAD_DIM, HEAD_DIM), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _expect(final_state, "final_state", torch.float32, (N, H, HEAD_DIM, HEAD_DIM))
+    lib = load_library()
+    if workspace is None:
+        nbytes = lib.kda_chunk_fwd_segmented_workspace_size(T, N, H, int(segments))
+        if nbytes == 0:
+            raise ValueError(f"invalid sizes T={T} N={N} H={H} segments={segments}")
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    st = lib.kda_chunk_fwd_segmented(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+        T, N, H, float(scale), int(segments), _ptr(o), _ptr(final_state), _ptr(workspace),
+        workspace.numel(), _stream(dev))
+    _check("kda_chunk_fwd_segmented", st)
     return o, final_state
 
 

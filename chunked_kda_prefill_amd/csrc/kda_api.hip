@@ -455,6 +455,62 @@ kda_status kda_chunk_fwd_fused(const void *q, const void *k, const void *v, cons
                         final_state, workspace, workspace_bytes, stream, pro);
 }
 
+// Workspace of the segmented forward: the plain workspace, then per chain
+// the exit state of segment 0 and the maps (M, b) of segments 1 .. P-2.
+static int64_t segmented_extra(int32_t N, int32_t H, int32_t segments) {
+  const int64_t per_chain = 1 + 2 * (int64_t)(segments > 2 ? segments - 2 : 0);
+  return (int64_t)N * H * per_chain * DK * DV * 4;
+}
+
+size_t kda_chunk_fwd_segmented_workspace_size(int64_t T, int32_t N, int32_t H, int32_t segments) {
+  if (check_sizes(T, N, H) != KDA_OK || segments < 1 || segments > KDA_MAX_SEGMENTS) return 0;
+  return (size_t)(align256(ws_layout(T, N, H).total) + segmented_extra(N, H, segments));
+}
+
+kda_status kda_chunk_fwd_segmented(const void *q, const void *k, const void *v, const float *g,
+                                   const float *beta, const float *initial_state,
+                                   const int32_t *cu_seqlens, int64_t T, int32_t N, int32_t H,
+                                   float scale, int32_t segments, void *o, float *final_state,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (segments < 1 || segments > KDA_MAX_SEGMENTS) return KDA_ERR_INVALID_ARGUMENT;
+  kda_status st = check_forward_args(q, k, v, g, beta, initial_state, cu_seqlens, T, N, H, o,
+                                     final_state, Prologue());
+  if (st != KDA_OK) return st;
+  Ws ws;
+  if ((st = carve(workspace, workspace_bytes, T, N, H, ws)) != KDA_OK) return st;
+  const int64_t base = align256(ws.L.total);
+  const int64_t total = base + segmented_extra(N, H, segments);
+  if ((int64_t)workspace_bytes < total) return KDA_ERR_WORKSPACE_TOO_SMALL;
+  const int64_t tok = T * H * DK;
+  const int64_t st_bytes = (int64_t)N * H * DK * DV * 4;
+  if (forward_inputs(q, k, v, g, beta, initial_state, cu_seqlens, T, N, H, nullptr, 0)
+          .hit(workspace, total) ||
+      overlap(workspace, total, o, tok * 2) || overlap(workspace, total, final_state, st_bytes))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if ((st = run_intra(q, k, v, g, beta, cu_seqlens, T, N, H, scale, ws, stream)) != KDA_OK)
+    return st;
+  if (segments == 1) return run_recurrence(initial_state, T, N, H, o, final_state, ws, stream);
+  RecurArgs ra;
+  ra.blocks = ws.blocks;
+  ra.chunk_first = ws.chunk_first;
+  ra.chunk_info = ws.chunk_info;
+  ra.h0 = initial_state;
+  ra.hT = final_state;
+  ra.o = static_cast<uint16_t *>(o);
+  ra.nc_max = ws.L.nc_max;
+  ra.T = T;
+  ra.N = N;
+  ra.H = H;
+  ra.segments = segments;
+  float *extra = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + base);
+  ra.xstate = extra;
+  ra.maps = extra + (int64_t)N * H * DK * DV;
+  ra.phase = 1;
+  if (launch_recurrence(ra, stream) != hipSuccess) return KDA_ERR_HIP;
+  ra.phase = 2;
+  return hip_status(launch_recurrence(ra, stream));
+}
+
 kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *g,
                                  const float *beta, const float *initial_state,
                                  const int32_t *cu_seqlens, int64_t T, int32_t N, int32_t H,

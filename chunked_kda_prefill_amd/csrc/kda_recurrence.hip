@@ -72,7 +72,13 @@ __device__ __forceinline__ void dma_round(__amdgpu_buffer_rsrc_t r, uint32_t vof
 // Buffer resource over one intermediate block, and the wave-uniform LDS
 // address of a block buffer.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t *blk) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(blk), 0, BLOCK_BYTES, BUF_DWORD3);
+  // the block address is wave-uniform: keep it in scalar registers even where
+  // the compiler computed it with vector instructions
+  const uint64_t a = (uint64_t)(uintptr_t)blk;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  uint8_t *u = reinterpret_cast<uint8_t *>((uintptr_t)(((uint64_t)hi << 32) | lo));
+  return __builtin_amdgcn_make_buffer_rsrc(u, 0, BLOCK_BYTES, BUF_DWORD3);
 }
 __device__ __forceinline__ uint32_t lds_base_of(const uint8_t *buf) {
   return __builtin_amdgcn_readfirstlane(lds_addr(buf));
@@ -195,6 +201,109 @@ __device__ __forceinline__ void copy_share(const uint8_t *src, uint8_t *dst, int
     copy_range<C, HALF, C::ROUNDS>(r, lbase, p, l);
 }
 
+// What one workgroup group computes: a whole chain (segments == 1), or one
+// run of a segment of a chain (the two phases of chunk-parallel state
+// passing, kda_recurrence.h).
+enum { INIT_H0 = 0, INIT_IDENTITY = 1, INIT_ZERO = 2, INIT_XSTATE = 3 };
+enum { EXIT_NONE = 0, EXIT_FINAL = 1, EXIT_XSTATE = 2, EXIT_MAP = 3 };
+struct RunDesc {
+  int64_t chain;  // -1: no run
+  int seg, init, exit, map, prefix;
+  bool use_u, write_o;
+};
+template <bool SEG>
+__device__ __forceinline__ RunDesc describe_run(const RecurArgs &a, int64_t run) {
+  const int64_t chains = (int64_t)a.N * a.H;
+  const int P = SEG ? a.segments : 1;
+  RunDesc d;
+  d.chain = -1;
+  d.seg = 0;
+  d.init = INIT_H0;
+  d.exit = EXIT_FINAL;
+  d.map = 0;
+  d.prefix = 0;
+  d.use_u = true;
+  d.write_o = true;
+  if (P <= 1) {
+    if (run < chains) d.chain = run;
+    return d;
+  }
+  if (a.phase == 1) {
+    // per chain: segment 0, then (M, b) of segments 1 .. P-2
+    const int64_t per = 1 + 2 * (int64_t)(P - 2);
+    if (run >= chains * per) return d;
+    d.chain = run / per;
+    const int r = (int)(run % per);
+    if (r == 0) {
+      d.exit = P == 1 ? EXIT_FINAL : EXIT_XSTATE;
+      return d;
+    }
+    d.seg = 1 + (r - 1) / 2;
+    d.map = (r - 1) % 2;  // 0: M (from the identity, U = 0); 1: b (from zero, U)
+    d.init = d.map == 0 ? INIT_IDENTITY : INIT_ZERO;
+    d.use_u = d.map == 1;
+    d.write_o = false;
+    d.exit = EXIT_MAP;
+    return d;
+  }
+  // phase 2: segments 1 .. P-1 from h_1 and the maps before them
+  const int64_t per = P - 1;
+  if (run >= chains * per) return d;
+  d.chain = run / per;
+  d.seg = 1 + (int)(run % per);
+  d.init = INIT_XSTATE;
+  d.prefix = d.seg;
+  d.exit = d.seg == P - 1 ? EXIT_FINAL : EXIT_NONE;
+  return d;
+}
+
+// S <- M S + b for a compute wave's state slice (value tiles nt0 .. nt0 +
+// TPW - 1, MFMA C layout).  M and b are fp32 [128][128] (key x key, key x
+// value) in global memory.  The product runs on bf16 MFMAs with both
+// operands split into hi + lo parts (hi.hi + hi.lo + lo.hi, ~16 mantissa
+// bits), A = M in the permuted k order of the state's B operands.
+template <int TPW>
+__device__ __forceinline__ void prefix_step(f32x4 (&S)[8][TPW], const float *M, const float *bv,
+                                            int nt0, int nn, int grp) {
+  bf16x8 bh[4][TPW], bl[4][TPW];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+    for (int q = 0; q < TPW; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = S[2 * s4 + (e >> 2)][q][e & 3];
+        split_bf16(x, bh[s4][q], bl[s4][q], e);
+      }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) acc[q] = zero4();
+    const float *row = M + (16 * t + nn) * DK;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const float4 lo4 = *reinterpret_cast<const float4 *>(row + 32 * s4 + 4 * grp);
+      const float4 hi4 = *reinterpret_cast<const float4 *>(row + 32 * s4 + 16 + 4 * grp);
+      const float av[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+      bf16x8 ah, al;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) split_bf16(av[e], ah, al, e);
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) {
+        acc[q] = mfma_bf16(ah, bh[s4][q], acc[q]);
+        acc[q] = mfma_bf16(ah, bl[s4][q], acc[q]);
+        acc[q] = mfma_bf16(al, bh[s4][q], acc[q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < TPW; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        S[t][q][r] = acc[q][r] + bv[(16 * t + 4 * grp + r) * DV + VCOL(nt0 + q, nn)];
+  }
+}
+
 }  // namespace
 
 // Kernel: PARTS workgroups per chain, NC + NCP waves each.  The NC compute
@@ -207,16 +316,21 @@ __device__ __forceinline__ void copy_share(const uint8_t *src, uint8_t *dst, int
 // intermediate blocks stream through two LDS buffers: while the waves compute
 // chunk c from one buffer, chunk c+1's block is copied global -> LDS into
 // the other by buffer_load_dwordx4 ... lds (no register staging).
-template <int NC, int NCP, int TPW>
+template <int NC, int NCP, int TPW, bool SEG>
 __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a) {
   using C = RecCfg<NC, NCP, TPW>;
   __shared__ __align__(16) uint8_t lds[2][BLOCK_BYTES];
   const int b = blockIdx.x;
   const int xcd = b & 7, i = b >> 3;
-  const int64_t chain = (int64_t)(i / C::PARTS) * 8 + xcd;
+  // run index: a chain, or (segments > 1) one run of a chain's segment
+  const int64_t run = (int64_t)(i / C::PARTS) * 8 + xcd;
   const int p = i % C::PARTS;
-  if (chain >= (int64_t)a.N * a.H) return;
-  const int s = (int)(chain / a.H), h = (int)(chain % a.H);
+  const int64_t chains = (int64_t)a.N * a.H;
+  const RunDesc rd = describe_run<SEG>(a, run);
+  if (rd.chain < 0) return;
+  const int64_t chain = rd.chain;
+  const int s = __builtin_amdgcn_readfirstlane((int)(chain / a.H));
+  const int h = __builtin_amdgcn_readfirstlane((int)(chain % a.H));
   const int tid = threadIdx.x;
   // The wave index lives in a scalar register, so that every branch on a
   // wave's role is a scalar jump.  MFMAs do not honour EXEC: under an
@@ -230,7 +344,18 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
   int64_t c_beg = chunk_first_of(a.chunk_first, s), c_end = chunk_first_of(a.chunk_first, s + 1);
   c_beg = c_beg < 0 ? 0 : (c_beg > nc_max ? nc_max : c_beg);
   c_end = c_end < c_beg ? c_beg : (c_end > nc_max ? nc_max : c_end);
+  if (SEG) {
+    // segment rd.seg of the chain: chunks [c_beg + seg m, c_beg + (seg + 1) m)
+    // (chunk indices < 2^31: nc_max H fits int32); wave-uniform scalars
+    const int n = (int)(c_end - c_beg);
+    const int m = (n + a.segments - 1) / a.segments;
+    const int s0 = (int)c_beg + rd.seg * m;
+    const int e0 = (int)c_end;
+    c_beg = __builtin_amdgcn_readfirstlane(s0 < e0 ? s0 : e0);
+    c_end = __builtin_amdgcn_readfirstlane(s0 + m < e0 ? s0 + m : e0);
+  }
   const int64_t st_base = ((int64_t)s * a.H + h) * DK * DV;
+  (void)chains;
   const uint8_t *chain_blocks = a.blocks + (int64_t)h * nc_max * BLOCK_BYTES;
 
   if (NCP > 0 && w >= NC) {
@@ -242,7 +367,8 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
     const int cw = w - NC;
     if (c_beg < c_end) copy_share<C, NCP>(chain_blocks + c_beg * BLOCK_BYTES, lds[0], cw, p, l);
     for (int64_t c = c_beg; c < c_end; ++c) {
-      if (c > c_beg + 1)
+      // the copy of this chunk is complete; o stores issued after it may not be
+      if (c > c_beg + 1 && rd.write_o)
         __builtin_amdgcn_s_waitcnt(OStore<C, NCP>::STORES | (0x7 << 4));
       else
         __builtin_amdgcn_s_waitcnt(0);
@@ -250,10 +376,10 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
       const int cur = (int)((c - c_beg) & 1);
       if (c + 1 < c_end)
         copy_share<C, NCP>(chain_blocks + (c + 1) * BLOCK_BYTES, lds[cur ^ 1], cw, p, l);
-      if (c > c_beg) store_o_staged<C, NCP>(a, lds[cur ^ 1], c - 1, h, p, cw, l);
+      if (c > c_beg && rd.write_o) store_o_staged<C, NCP>(a, lds[cur ^ 1], c - 1, h, p, cw, l);
     }
     __syncthreads();  // the compute waves have staged the last chunk's o
-    if (c_end > c_beg)
+    if (c_end > c_beg && rd.write_o)
       store_o_staged<C, NCP>(a, lds[(int)((c_end - 1 - c_beg) & 1)], c_end - 1, h, p, cw, l);
     // no copy may still be writing LDS when the workgroup ends
     __builtin_amdgcn_s_waitcnt(0);
@@ -263,6 +389,8 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
   // ---- compute waves ----
   // state slice: key tiles t = 0..7, value tiles nt0 + q
   f32x4 S[8][TPW];
+  const float *init = rd.init == INIT_H0 ? (a.h0 ? a.h0 + st_base : nullptr)
+                      : rd.init == INIT_XSTATE ? a.xstate + chain * DK * DV : nullptr;
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -271,8 +399,14 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * t + 4 * grp + r;
         const int col = VCOL(nt0 + q, nn);
-        S[t][q][r] = a.h0 ? a.h0[st_base + row * DV + col] : 0.f;
+        S[t][q][r] = init ? init[row * DV + col] : (rd.init == INIT_IDENTITY && row == col ? 1.f : 0.f);
       }
+  // phase 2: the entry state of segment seg from h_1 through the maps of
+  // segments 1 .. seg - 1
+  for (int q2 = 1; SEG && q2 < rd.prefix; ++q2) {
+    const float *M = a.maps + ((chain * (a.segments - 2) + (q2 - 1)) * 2) * DK * DV;
+    prefix_step<TPW>(S, M, M + DK * DV, nt0, nn, grp);
+  }
 
   if (NCP == 0 && c_beg < c_end) {
 #pragma unroll
@@ -343,7 +477,7 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
       for (int q = 0; q < TPW; ++q) {
         const bf16x4 u = *reinterpret_cast<const bf16x4 *>(blk + U_OFFSET(nt0 + q, mt, l));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vn[mt][q][r] = (float)u[r];
+        for (int r = 0; r < 4; ++r) vn[mt][q][r] = rd.use_u ? (float)u[r] : 0.f;
         ot[mt][q] = zero4();
       }
 
@@ -368,7 +502,7 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
     for (int s4 = 0; s4 < 4; ++s4) {
       // one token tile of last chunk's o (and, without copy waves, a quarter
       // of the next chunk's copy)
-      if (NCP == 0 && c > c_beg) store_o_tile(s4);
+      if (NCP == 0 && c > c_beg && rd.write_o) store_o_tile(s4);
       if (NCP == 0 && c + 1 < c_end)
         copy_step<C>(chain_blocks + (c + 1) * BLOCK_BYTES, lds[cur ^ 1], w, p, l, s4);
       bf16x8 nw[4], nq[4];
@@ -388,10 +522,13 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int q = 0; q < TPW; ++q) {
-          vn[mt][q] = mfma_bf16(fw[mt], hb[s4][q], vn[mt][q]);
-          ot[mt][q] = mfma_bf16(hb[s4][q], fq[mt], ot[mt][q]);
-        }
+        for (int q = 0; q < TPW; ++q) vn[mt][q] = mfma_bf16(fw[mt], hb[s4][q], vn[mt][q]);
+      if (rd.write_o) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int q = 0; q < TPW; ++q) ot[mt][q] = mfma_bf16(hb[s4][q], fq[mt], ot[mt][q]);
+      }
       if (s4 < 3) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -424,12 +561,14 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
         for (int q = 0; q < TPW; ++q) S[t][q] = mfma_bf16(fk[s2][t], vb[s2][q], S[t][q]);
 
     // o^T += v_new^T Aqk^T
+    if (rd.write_o) {
 #pragma unroll
-    for (int x = 0; x < AQK_FRAGS; ++x)
+      for (int x = 0; x < AQK_FRAGS; ++x)
 #pragma unroll
-      for (int q = 0; q < TPW; ++q) {
-        ot[lt_mt(x)][q] = mfma_bf16(vb[lt_s(x)][q], fa[x], ot[lt_mt(x)][q]);
-      }
+        for (int q = 0; q < TPW; ++q) {
+          ot[lt_mt(x)][q] = mfma_bf16(vb[lt_s(x)][q], fa[x], ot[lt_mt(x)][q]);
+        }
+    }
 
     // o^T of this chunk as bf16 (nearest even), stored during the next one:
     // by the copy waves from LDS, or (without them) by this wave
@@ -439,7 +578,7 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
       for (int q = 0; q < TPW; ++q)
 #pragma unroll
         for (int r = 0; r < 4; ++r) o_pend[mt][q][r] = (bf16_t)ot[mt][q][r];
-    if (NCP > 0) {
+    if (NCP > 0 && rd.write_o) {
       uint8_t *ost = lds[cur] + o_stage_off<C>(p);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -455,12 +594,17 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
   if (NCP > 0) {
     __builtin_amdgcn_s_waitcnt(LGKM_ONLY);
     __syncthreads();  // the copy waves store the last chunk's o
-  } else if (c_end > c_beg) {
+  } else if (c_end > c_beg && rd.write_o) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) store_o_tile(mt);
   }
 
-  if (a.hT) {
+  float *exit_state = rd.exit == EXIT_FINAL ? (a.hT ? a.hT + st_base : nullptr)
+                      : rd.exit == EXIT_XSTATE ? a.xstate + chain * DK * DV
+                      : rd.exit == EXIT_MAP
+                          ? a.maps + ((chain * (a.segments - 2) + (rd.seg - 1)) * 2 + rd.map) * DK * DV
+                          : nullptr;
+  if (exit_state) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -469,7 +613,7 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * t + 4 * grp + r;
           const int col = VCOL(nt0 + q, nn);
-          a.hT[st_base + row * DV + col] = S[t][q][r];
+          exit_state[row * DV + col] = S[t][q][r];
         }
   }
   // no copy may still be writing LDS when the workgroup ends
@@ -477,26 +621,34 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
 }
 
 template <int NC, int NCP, int TPW>
-static hipError_t launch_rec(const RecurArgs &a, int64_t chains, hipStream_t stream) {
+static hipError_t launch_rec(const RecurArgs &a, int64_t runs, hipStream_t stream) {
   using C = RecCfg<NC, NCP, TPW>;
-  const int64_t groups = (chains + 7) / 8;  // chains per XCD slot, rounded up
+  const int64_t groups = (runs + 7) / 8;  // runs per XCD slot, rounded up
   const int64_t grid = groups * 8 * C::PARTS;
-  hipLaunchKernelGGL((recurrence_kernel<NC, NCP, TPW>), dim3((unsigned)grid), dim3(C::THREADS), 0,
-                     stream, a);
+  if (a.segments > 1)
+    hipLaunchKernelGGL((recurrence_kernel<NC, NCP, TPW, true>), dim3((unsigned)grid),
+                       dim3(C::THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((recurrence_kernel<NC, NCP, TPW, false>), dim3((unsigned)grid),
+                       dim3(C::THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_recurrence(const RecurArgs &a, hipStream_t stream) {
   const int64_t chains = (int64_t)a.N * a.H;
   if (chains <= 0) return hipSuccess;
+  // runs of this launch (describe_run): chains, or the runs of a phase
+  int64_t runs = chains;
+  if (a.segments > 1)
+    runs = a.phase == 1 ? chains * (1 + 2 * (int64_t)(a.segments - 2)) : chains * (a.segments - 1);
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  // split each chain over as many workgroups as still fit the device once
-  if (chains * 4 <= cus) return launch_rec<2, 2, 1>(a, chains, stream);
-  if (chains * 2 <= cus) return launch_rec<4, 2, 1>(a, chains, stream);
-  return launch_rec<4, 0, 2>(a, chains, stream);
+  // split each run over as many workgroups as still fit the device once
+  if (runs * 4 <= cus) return launch_rec<2, 2, 1>(a, runs, stream);
+  if (runs * 2 <= cus) return launch_rec<4, 2, 1>(a, runs, stream);
+  return launch_rec<4, 0, 2>(a, runs, stream);
 }
 
 }  // namespace kda

@@ -107,6 +107,38 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
                          hipStream_t stream);
 
 /*
+ * Chunk-parallel state passing (derived from the chunk recurrence of the KDA
+ * TPU report, section 6.2: each chunk maps the state affinely, h' = A_c h +
+ * B_c with A_c = Diag(gamma) - kg^T W and B_c = kg^T U, so a run of chunks
+ * composes into h' = M h + b).  The same operation as kda_chunk_fwd, for
+ * few, long chains: each (sequence, head) chain of n chunks is cut into
+ * `segments` runs of ceil(n / segments) chunks.  A first recurrence pass
+ * runs segment 0 from the initial state and, in parallel, every middle
+ * segment twice, from the identity with U = 0 (giving M) and from zero
+ * (giving b); a second pass runs every later segment from its entry state,
+ * h_p = M_{p-1} h_{p-1} + b_{p-1} (products on bf16 MFMAs with hi + lo
+ * operands).  Three chain-lengths of recurrence work are done instead of
+ * one, in about two segment-lengths of latency.
+ *
+ *   segments   1 .. KDA_MAX_SEGMENTS; 1 is kda_chunk_fwd itself.
+ *   workspace  >= kda_chunk_fwd_segmented_workspace_size(T, N, H, segments)
+ *              bytes, 256-byte aligned.
+ * Everything else as kda_chunk_fwd.  Results differ from kda_chunk_fwd's by
+ * rounding only.  A sequence's results depend on its own tokens, its
+ * initial state and `segments`, not on its neighbours or offset.
+ */
+#define KDA_MAX_SEGMENTS 64
+size_t kda_chunk_fwd_segmented_workspace_size(int64_t T, int32_t N, int32_t H,
+                                              int32_t segments);
+kda_status kda_chunk_fwd_segmented(const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta,
+                                   const float *initial_state, const int32_t *cu_seqlens,
+                                   int64_t T, int32_t N, int32_t H, float scale,
+                                   int32_t segments, void *o, float *final_state,
+                                   void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/*
  * kda_chunk_fwd without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation.  The workspace is a file-scope device

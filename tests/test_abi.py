@@ -281,3 +281,30 @@ def test_noalloc_entry_checks_before_any_device_call():
     assert call(q=None) == INV
     assert call(T=-1) == INV
     assert call(o=(1 << 20) + 64) == INV                      # o over q
+
+
+def test_segmented_entry_rejects_bad_arguments():
+    lib = kda.load_library()
+    A = 1 << 20
+    assert lib.kda_chunk_fwd_segmented_workspace_size(2048, 1, 16, 0) == 0
+    assert lib.kda_chunk_fwd_segmented_workspace_size(2048, 1, 16, 65) == 0
+    plain = kda.workspace_size(2048, 1, 16)
+    need = lib.kda_chunk_fwd_segmented_workspace_size(2048, 1, 16, 4)
+    # segment 0's exit state and two maps (M, b) per chain for the middle segments
+    assert need >= plain + 16 * (1 + 2 * 2) * 128 * 128 * 4
+    assert lib.kda_chunk_fwd_segmented_workspace_size(2048, 1, 16, 1) >= plain
+
+    def call(segments=4, ws_bytes=0, **over):
+        a = dict(q=A, k=2 * A, v=3 * A, g=4 * A, beta=5 * A, h0=None, cu=6 * A, T=128, N=1, H=2,
+                 o=7 * A, hT=8 * A, ws=64 * A)
+        a.update(over)
+        return lib.kda_chunk_fwd_segmented(a["q"], a["k"], a["v"], a["g"], a["beta"], a["h0"],
+                                           a["cu"], a["T"], a["N"], a["H"], 1.0, segments,
+                                           a["o"], a["hT"], a["ws"], ws_bytes, None)
+    assert call(segments=0) == 1
+    assert call(segments=65) == 1
+    assert call(q=None) == 1
+    assert call() == 3                                         # workspace too small
+    small = lib.kda_chunk_fwd_segmented_workspace_size(128, 1, 2, 4)
+    assert call(ws_bytes=small - 1) == 3
+    assert call(ws_bytes=small, cu=64 * A + 256) == 1          # workspace over an input
