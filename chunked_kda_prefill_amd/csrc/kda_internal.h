@@ -3,7 +3,8 @@
 // Geometry: K = V = 128 head dims, BT = 64-token chunks, SB = 16-token
 // subblocks (KDA TPU report, sections 1 and 4).  Every matrix product runs on
 // v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 accumulate) except the
-// 16x16 triangular inverses, which use v_mfma_f32_16x16x4_f32.
+// 16x16 triangular inverses, which use v_mfma_f32_16x16x16_bf16 on hi + lo
+// operand splits.
 //
 // MFMA lane layout used throughout (wave64, lane l, n = l & 15, grp = l >> 4):
 //   A fragment  (16 x 32, bf16x8):  A[row = n][k = 8*grp + e],   e = 0..7
@@ -126,9 +127,6 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 // exp(x) for natural-log x: one multiply and the hardware base-2 exponential.
 __device__ __forceinline__ float exp_nat(float x) {

@@ -43,7 +43,9 @@
 // (I + X)(I + X^2)(I + X^4)(I + X^8), X = -L_aa, exact because X is strictly
 // lower (X^16 = 0); then wave b fills column b of T top-down,
 // T_ab = -T_aa sum_{c=b}^{a-1} L_ac T_cb, needing only the other waves'
-// diagonal blocks.  All of it runs in fp32 on v_mfma_f32_16x16x4_f32.
+// diagonal blocks.  L and T stay fp32; each 16 x 16 product runs on three
+// v_mfma_f32_16x16x16_bf16 with hi + lo bf16 operand splits (~16 mantissa
+// bits per product, shorter dependent chains than fp32 MFMAs).
 #include "kda_chunk_table.h"
 #include "kda_cumsum.h"
 #include "kda_internal.h"
@@ -164,13 +166,30 @@ __device__ __forceinline__ void pin(T &x) {
   asm volatile("" : "+v"(x));
 }
 
-// 16 x 16 x 16 fp32 product from C-layout registers: At holds A^T and B holds
-// B (lane (nn, grp), element r = row 4grp + r, column nn); k runs over
-// 4 grp + s.  Returns acc + A B in the same layout.
-__device__ __forceinline__ f32x4 mm16(const f32x4 &At, const f32x4 &B, f32x4 acc) {
+// 16 x 16 x 16 product from C-layout registers: At holds A^T and B holds B
+// (lane (nn, grp), element r = row 4grp + r, column nn), which are exactly
+// the operand lanes of v_mfma_f32_16x16x16_bf16 (lane (nn, grp) supplies
+// k = 4 grp + r); returns acc + A B in the same layout.  Each operand is split
+// into hi + lo bf16 parts and the product is hi.hi + hi.lo + lo.hi (the lo.lo
+// term, < 2^-16 of |A||B|, dropped): three short MFMAs, whose dependent
+// chains are shorter than those of four fp32 16x16x4 MFMAs.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+struct Split4 {
+  s16x4 hi, lo;
+};
+__device__ __forceinline__ Split4 split4(const f32x4 &x) {
+  bf16x4 h, l;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) acc = mfma_f32(At[s], B[s], acc);
-  return acc;
+  for (int e = 0; e < 4; ++e) {
+    h[e] = (bf16_t)x[e];
+    l[e] = (bf16_t)(x[e] - (float)h[e]);
+  }
+  return Split4{__builtin_bit_cast(s16x4, h), __builtin_bit_cast(s16x4, l)};
+}
+__device__ __forceinline__ f32x4 mm16s(const Split4 &At, const Split4 &B, f32x4 acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(At.lo, B.hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(At.hi, B.lo, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(At.hi, B.hi, acc, 0, 0, 0);
 }
 
 }  // namespace
@@ -310,6 +329,11 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(blk, 0, BLOCK_BYTES, BUF_DWORD3);
   const int lv16 = 16 * l;  // lane offset of a fragment store
   float *rt = sm.tt;  // [0, 4 DK): reference rows; [4 DK, 8 DK): subblock totals
+  // per-channel factor tables for the factor phase, in the part of tt that
+  // the row fragments of subblock 3 (below) leave free: scale * R_a, and
+  // the reference rows times log2(e)
+  float *srt = sm.tt + 24 * DK;  // [4][DK]
+  float *r7l = sm.tt + 28 * DK;  // [4][DK]
 
   // ---- subblock cumsum down the wave's 16 rows; publish the reference row
   // and the total of each subblock.  (The previous unit last read tt, beta
@@ -341,13 +365,17 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
     if (tid < DK) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        sm.tab[TAB_R + b][ch] = exp_nat(Gr[b]);
+        const float R = exp_nat(Gr[b]);
+        sm.tab[TAB_R + b][ch] = R;
+        srt[b * DK + ch] = a.scale * R;
         sm.tab[TAB_Q + b][ch] = exp_nat(acc - Gr[b]);
       }
     } else {
 #pragma unroll
       for (int p = 0; p < 6; ++p) sm.tab[TAB_C + p][ch] = exp_nat(Gr[OFF_A[p]] - Gr[OFF_B[p]]);
       sm.tab[TAB_GAM][ch] = exp_nat(acc);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) r7l[b * DK + ch] = rt[b * DK + ch] * LOG2E;
     }
   }
 
@@ -403,12 +431,15 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
     for (int hh = 0; hh < 2; ++hh) {
       const int j = 2 * s + hh;
       const int ch = slot_ch(j, grp);
-      const float4 r7 = *reinterpret_cast<const float4 *>(&rt[w * DK + ch]);
+      const float4 r7 = *reinterpret_cast<const float4 *>(&r7l[w * DK + ch]);
       const float4 R = *reinterpret_cast<const float4 *>(&sm.tab[TAB_R + w][ch]);
+      const float4 SR = *reinterpret_cast<const float4 *>(&srt[w * DK + ch]);
       const float4 Q = *reinterpret_cast<const float4 *>(&sm.tab[TAB_Q + w][ch]);
       const float rv[4] = {R.x, R.y, R.z, R.w};
+      const float sv[4] = {SR.x, SR.y, SR.z, SR.w};
       const float qv[4] = {Q.x, Q.y, Q.z, Q.w};
-      const float d[4] = {G[j].x - r7.x, G[j].y - r7.y, G[j].z - r7.z, G[j].w - r7.w};
+      const float gv[4] = {G[j].x, G[j].y, G[j].z, G[j].w};
+      const float rl[4] = {r7.x, r7.y, r7.z, r7.w};
       float qf[4], kf[4], kgv[4], kmv[4], ktv[4];
       unpack4(qs[j], qf);
       unpack4(ks[j], kf);
@@ -421,10 +452,11 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float t = d[e] * LOG2E;
+        // (G_i - G_ref) log2(e) in one rounding step
+        const float t = fmaf(gv[e], LOG2E, -rl[e]);
         const float e1 = __builtin_amdgcn_exp2f(t), e2 = __builtin_amdgcn_exp2f(-t);
         const float qe = qf[e] * e1, ke = kf[e] * e1, kt = kf[e] * e2;
-        f[4 * hh + e] = (bf16_t)(a.scale * rv[e] * qe);
+        f[4 * hh + e] = (bf16_t)(sv[e] * qe);
         qh[s][4 * hh + e] = (bf16_t)qe;
         kh[s][4 * hh + e] = (bf16_t)ke;
         kth[4 * hh + e] = (bf16_t)kt;
@@ -573,9 +605,9 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
 
   // ---- diagonal block w of T: Neumann product in registers ----
   // Every 16 x 16 matrix M lives in MFMA C layout (lane (nn, grp) holds
-  // M[4grp + r][nn], r = 0..3), next to its transpose.  With the k order
-  // k = 4 grp + s, a product A B is  sum_s mfma(At[s], B[s])  for A^T and B
-  // in that layout, so the chain needs no LDS round trips.
+  // M[4grp + r][nn], r = 0..3), next to its transpose.  A product A B takes
+  // A^T and B in that layout as MFMA operands (mm16s), so the chain needs no
+  // LDS round trips.
   const int d0 = SB * w;
   f32x4 PC;  // T_ww
   {
@@ -592,11 +624,13 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
     }
 #pragma unroll
     for (int it = 0; it < 3; ++it) {
-      const f32x4 Y2C = mm16(YtC, YC, zero4());    // Y Y
-      const f32x4 PnC = mm16(PtC, Y2C, PC);        // P + P Y^2
+      const Split4 sY = split4(YC), sYt = split4(YtC), sPt = split4(PtC);
+      const f32x4 Y2C = mm16s(sYt, sY, zero4());   // Y Y
+      const Split4 sY2 = split4(Y2C);
+      const f32x4 PnC = mm16s(sPt, sY2, PC);       // P + P Y^2
       if (it < 2) {
-        const f32x4 Y2tC = mm16(YC, YtC, zero4());  // Y^T Y^T
-        PtC = mm16(Y2C, PtC, PtC);                  // P^T + (Y^2)^T P^T
+        const f32x4 Y2tC = mm16s(sY, sYt, zero4());  // Y^T Y^T
+        PtC = mm16s(sY2, sPt, PtC);                  // P^T + (Y^2)^T P^T
         YC = Y2C;
         YtC = Y2tC;
       }
@@ -612,8 +646,8 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   // ---- column w of T below the diagonal, top-down:
   // T_ab = -T_aa sum_{c=b}^{a-1} L_ac T_cb  with b = w, a = w + o ----
   {
-    f32x4 TC[4];
-    TC[0] = PC;
+    Split4 sT[4];  // the column's blocks T_{w+o, w} as split operands
+    sT[0] = split4(PC);
 #pragma unroll
     for (int o = 1; o < 4; ++o) {
       if (w + o < 4) {
@@ -624,15 +658,16 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
           // A = L_ac: its transpose in C layout is row nn, 4 consecutive columns
           const float4 lr =
               *reinterpret_cast<const float4 *>(&sm.lt[sw_lt(SB * ba + nn, SB * (w + oc) + 4 * grp)]);
-          MC = mm16(as_f32x4(lr), TC[oc], MC);
+          MC = mm16s(split4(as_f32x4(lr)), sT[oc], MC);
         }
         const float4 tr = *reinterpret_cast<const float4 *>(&sm.tt[sw_lt(SB * ba + nn, SB * ba + 4 * grp)]);
-        const f32x4 TabC = mm16(as_f32x4(tr), MC, zero4());
+        f32x4 TabC = mm16s(split4(as_f32x4(tr)), split4(MC), zero4());
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          TC[o][r] = -TabC[r];
-          sm.tt[sw_lt(SB * ba + 4 * grp + r, SB * w + nn)] = -TabC[r];
+          TabC[r] = -TabC[r];
+          sm.tt[sw_lt(SB * ba + 4 * grp + r, SB * w + nn)] = TabC[r];
         }
+        sT[o] = split4(TabC);
       }
     }
   }
