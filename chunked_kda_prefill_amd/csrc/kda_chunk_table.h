@@ -8,7 +8,9 @@
 //
 // chunk_table_build() is run by one 256-thread workgroup: the standalone
 // chunk-table kernel, or every workgroup of the intra-chunk kernel when the
-// batch is small enough to keep the per-sequence chunk offsets in LDS.
+// batch is small enough to keep the per-sequence chunk offsets in LDS.  Up to
+// 64 sequences, one wave builds it with a shuffle scan and no barriers but
+// the last (every workgroup of the intra kernel pays this prologue).
 #pragma once
 
 #include "kda_internal.h"
@@ -40,6 +42,61 @@ __device__ __forceinline__ void chunk_table_build(const int32_t *__restrict__ cu
                                                   int32_t *__restrict__ flags, int32_t *first_lds,
                                                   TableScratch &sc) {
   const int tid = threadIdx.x;
+  if (N <= 64) {
+    // Up to 64 sequences: one wave, one sequence per lane, the scan across
+    // lanes by shuffles; the other waves only meet the closing barrier.
+    if (tid < 64) {
+      const int s = tid;
+      int64_t cnt = 0, a = 0, L = 0;
+      bool bad = false;
+      if (s < N) {
+        const int64_t a_raw = cu[s], b_raw = cu[s + 1];
+        a = table_clamp(a_raw, T);
+        const int64_t b = table_clamp(b_raw, T);
+        L = b > a ? b - a : 0;
+        cnt = (L + BT - 1) / BT;
+        bad = (a != a_raw) || (b != b_raw) || (b_raw < a_raw);
+        if (s == 0 && a_raw != 0) bad = true;
+        if (s == N - 1 && b_raw != T) bad = true;
+      }
+      int64_t incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t up = __shfl_up(incl, off, 64);
+        if (s >= off) incl += up;
+      }
+      const int64_t first = incl - cnt;
+      const int64_t total = __shfl(incl, 63, 64);
+      const int64_t nc = total < nc_max ? total : nc_max;
+      if (s < N) {
+        const int32_t f = (int32_t)(first < nc_max ? first : nc_max);
+        if (first_lds) first_lds[s] = f;
+        if (write) {
+          chunk_first[s] = f;
+          for (int64_t j = 0; j < cnt; ++j) {
+            const int64_t c = first + j;
+            if (c >= nc_max) {
+              bad = true;
+              break;
+            }
+            const int64_t len = L - j * BT < BT ? L - j * BT : BT;
+            chunk_info[c] = make_int4((int)(a + j * BT), (int)len, (int)s, (int)j);
+          }
+        }
+      }
+      if (s == 0) {
+        if (first_lds) first_lds[N] = (int32_t)nc;
+        if (write) chunk_first[N] = (int32_t)nc;
+      }
+      if (write) {
+        for (int64_t c = nc + s; c < nc_max; c += 64) chunk_info[c] = make_int4(0, 0, -1, -1);
+        const bool any_bad = __any(bad);
+        if (s == 0) flags[0] = any_bad ? 1 : 0;
+      }
+    }
+    __syncthreads();
+    return;
+  }
   if (tid == 0) {
     sc.carry = 0;
     sc.bad = 0;
