@@ -208,10 +208,23 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 // [T, H, 128] tensor.  A lane whose row is past n addresses beyond the
 // record count, so the hardware range check returns zeros for it: rows past
 // a partial chunk's end load as q = k = v = g = beta = 0 with no masking.
+//
+// A unit's record is wave-uniform, but where it comes from LDS (the inline
+// chunk table) the compiler cannot prove it: a resource it then keeps in
+// vector registers is used through a waterfall loop whose s_waitcnt
+// vmcnt(0) waits for every load and store still in flight (measured: ~30% of
+// a unit's time).  readfirstlane puts base and size in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *base, int bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((uintptr_t)(((uint64_t)hi << 32) | lo)),
+                                           0, __builtin_amdgcn_readfirstlane(bytes), BUF_DWORD3);
+}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_rsrc(const void *base, int64_t tb, int n,
                                                              int H, int h, int elem) {
   const char *p = static_cast<const char *>(base) + ((tb * H + h) * DK) * elem;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), 0, n * H * DK * elem, BUF_DWORD3);
+  return uniform_rsrc(p, n * H * DK * elem);
 }
 
 // bf16 rows are read 16 bytes per lane: for key slab s (32 channels) lane
@@ -235,7 +248,7 @@ struct UnitInputs {
   int n;
   u32x4 q[4], k[4];  // per key slab: channels 32 s + 8 load_m(grp) + 0..7
   float4 g[8];       // channels slot_ch(j, grp) + 0..3
-  float beta;
+  uint32_t beta;     // bits: fp32 beta, or bf16 beta logit (zero-extended)
 };
 
 // Issues the loads (every lane loads, back to back, without branches; rows
@@ -259,14 +272,13 @@ __device__ __forceinline__ void load_unit(const IntraArgs &a, const int4 info, i
     if (a.b) {
       // beta logits (bf16) of a strided slice; the sigmoid is taken where
       // beta is published (rows past n read 0 here and are set to 0 there)
-      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t *>(a.b + tb * a.b_stride + h), 0, (int)(n * a.b_stride * 2), BUF_DWORD3);
-      in.beta = bf16_bits_to_f32(
-          __builtin_amdgcn_raw_buffer_load_b16(rb, (int)(2 * row * a.b_stride), 0, AUX_G));
+      const __amdgpu_buffer_rsrc_t rb = uniform_rsrc(a.b + tb * a.b_stride + h, (int)(n * a.b_stride * 2));
+      // raw bits: converted where they are used, so that no wait for this
+      // load is placed right after it
+      in.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)(2 * row * a.b_stride), 0, AUX_G);
     } else {
-      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float *>(a.beta + tb * a.H + h), 0, n * a.H * 4, BUF_DWORD3);
-      in.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * row * a.H, 0, AUX_G));
+      const __amdgpu_buffer_rsrc_t rb = uniform_rsrc(a.beta + tb * a.H + h, n * a.H * 4);
+      in.beta = __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * row * a.H, 0, AUX_G);
     }
   }
   if (part < 0 || part == 1) {
@@ -350,7 +362,9 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
     for (int j = 0; j < 8; ++j)
       *reinterpret_cast<float4 *>(&rt[(4 + w) * DK + slot_ch(j, grp)]) = G[j];
   }
-  if (grp == 0) sm.beta[row] = a.b ? (row < n ? 1.f / (1.f + expf(-in.beta)) : 0.f) : in.beta;
+  if (grp == 0)
+    sm.beta[row] = a.b ? (row < n ? 1.f / (1.f + expf(-bf16_bits_to_f32((uint16_t)in.beta))) : 0.f)
+                       : __uint_as_float(in.beta);
   __syncthreads();
 
   // ---- per-channel tables (two threads per channel) ----
