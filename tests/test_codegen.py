@@ -226,3 +226,52 @@ def test_recurrence_m0_is_preserved(tmp_path):
     assert "lds" in asm
     bad = m0_writes_outside_dma(asm)
     assert not bad, f"M0 written outside the save/restore DMA sequence at lines {bad[:10]}"
+
+
+def waterfall_loops(asm: str) -> list:
+    """Line numbers of vector memory instructions issued from inside a
+    waterfall loop: a loop whose body reads a value with v_readfirstlane,
+    narrows EXEC to the lanes that match it, issues the access and clears
+    those lanes (s_xor_b64 exec, exec, ...) before branching back while any
+    remain.  The compiler emits one when a buffer resource or scalar operand
+    lives in vector registers; its s_waitcnt vmcnt(0) then waits for every
+    load and store in flight."""
+    ins = _instructions(asm)
+    labels = {text[:-1]: k for k, (_, op, text) in enumerate(ins) if text.endswith(":")}
+    bad = []
+    for k, (ln, op, text) in enumerate(ins):
+        if op != "s_cbranch_execnz":
+            continue
+        target = labels.get(text.split()[1])
+        if target is None or target > k:
+            continue
+        body = ins[target + 1:k]
+        ops = [b[1] for b in body]
+        if ("v_readfirstlane_b32" in ops and any(o.startswith("s_and_saveexec") for o in ops)
+                and any(b[2].startswith("s_xor_b64 exec, exec") for b in body)):
+            bad += [b[0] for b in body if b[1].startswith(("buffer_", "global_"))]
+    return bad
+
+
+def test_waterfall_scanner():
+    asm = "\n".join([
+        ".LBB0_5:",
+        "  v_readfirstlane_b32 s36, v36",
+        "  s_waitcnt vmcnt(0)",
+        "  v_cmp_eq_u64_e32 vcc, s[36:37], v[36:37]",
+        "  s_and_saveexec_b64 s[0:1], vcc",
+        "  buffer_load_dword v0, v38, s[36:39], 0 offen",   # 6
+        "  s_xor_b64 exec, exec, s[0:1]",
+        "  s_cbranch_execnz .LBB0_5",
+        "  s_endpgm"])
+    assert waterfall_loops(asm) == [6]
+    # a forward if/else over EXEC is not a loop
+    assert waterfall_loops(asm.replace(".LBB0_5:\n", "").replace("  s_endpgm", ".LBB0_5:\n  s_endpgm")) == []
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None, reason="hipcc not available")
+@pytest.mark.parametrize("src", KERNELS)
+def test_no_waterfall_loops(src, tmp_path):
+    asm, _ = _compile(src, tmp_path)
+    bad = waterfall_loops(asm)
+    assert not bad, f"{src}: memory access inside a waterfall loop at assembly lines {bad[:10]}"
