@@ -35,10 +35,10 @@ def _instructions(asm: str):
     """(line number, opcode, text) of instructions and labels, in order."""
     out = []
     for i, line in enumerate(asm.split("\n")):
-        s = line.strip()
-        if not s or s.startswith(";") or (s.startswith(".") and not s.endswith(":")):
+        # comments first: the compiler annotates labels (".LBB1_5:  ; in Loop")
+        s = line.split(";")[0].strip()
+        if not s or (s.startswith(".") and not s.endswith(":")):
             continue
-        s = s.split(";")[0].strip()
         out.append((i + 1, s.split()[0], s))
     return out
 
