@@ -46,6 +46,8 @@
 // diagonal blocks.  L and T stay fp32; each 16 x 16 product runs on three
 // v_mfma_f32_16x16x16_bf16 with hi + lo bf16 operand splits (~16 mantissa
 // bits per product, shorter dependent chains than fp32 MFMAs).
+#include <type_traits>
+
 #include "kda_chunk_table.h"
 #include "kda_cumsum.h"
 #include "kda_internal.h"
@@ -570,34 +572,46 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
       accA = mfma_bf16(bh, rqh, accA);
       accL = mfma_bf16(rkh, bh, accL);
     };
-    // first block: (ba0, bb0) with the row side in registers or LDS
-    const int ba0 = (w == 0) ? 3 : w, bb0 = (w == 3) ? 2 : 0;
-    const bool row0_lds = (w == 0);
-    // second block (waves 1, 2): (3,1) from LDS rows, or (2,1) own rows
-    const bool two = (w == 1) || (w == 2);
-    const int ba1 = (w == 1) ? 3 : 2, bb1 = 1;
-    const bool row1_lds = (w == 1);
+    // One straight-line loop per wave role (the role branch is taken once,
+    // outside it), so that the LDS reads of later k-steps can be issued
+    // ahead of the earlier steps' MFMAs.  First block (ba0, bb0), second
+    // block (ba1, bb1) for waves 1 and 2; the row side is the wave's own
+    // registers, or subblock 3's fragments from LDS.
     f32x4 accA0 = zero4(), accL0 = zero4(), accA1 = zero4(), accL1 = zero4();
+    auto blocks = [&](auto first_lds, auto second, auto second_lds, int ba0, int bb0, int ba1,
+                      int bb1) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 bh;
-      col_frag(ba0, bb0, s, bh);
-      if (row0_lds)
-        step(bh, rowf[(s * 2 + 0) * 64 + l], rowf[(s * 2 + 1) * 64 + l], accA0, accL0);
-      else
-        step(bh, qh[s], kh[s], accA0, accL0);
-      if (two) {
-        bf16x8 ch_;
-        col_frag(ba1, bb1, s, ch_);
-        if (row1_lds)
-          step(ch_, rowf[(s * 2 + 0) * 64 + l], rowf[(s * 2 + 1) * 64 + l], accA1, accL1);
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 bh;
+        col_frag(ba0, bb0, s, bh);
+        if constexpr (decltype(first_lds)::value)
+          step(bh, rowf[(s * 2 + 0) * 64 + l], rowf[(s * 2 + 1) * 64 + l], accA0, accL0);
         else
-          step(ch_, qh[s], kh[s], accA1, accL1);
+          step(bh, qh[s], kh[s], accA0, accL0);
+        if constexpr (decltype(second)::value) {
+          bf16x8 ch_;
+          col_frag(ba1, bb1, s, ch_);
+          if constexpr (decltype(second_lds)::value)
+            step(ch_, rowf[(s * 2 + 0) * 64 + l], rowf[(s * 2 + 1) * 64 + l], accA1, accL1);
+          else
+            step(ch_, qh[s], kh[s], accA1, accL1);
+        }
       }
-    }
-    f32x4 unused;
-    strip_out(ba0, bb0, accA0, accL0, unused, false);
-    if (two) strip_out(ba1, bb1, accA1, accL1, unused, false);
+      f32x4 unused;
+      strip_out(ba0, bb0, accA0, accL0, unused, false);
+      if constexpr (decltype(second)::value) strip_out(ba1, bb1, accA1, accL1, unused, false);
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    //   wave 0: (3,0)   wave 1: (1,0) (3,1)   wave 2: (2,0) (2,1)   wave 3: (3,2)
+    if (w == 0)
+      blocks(yes{}, no{}, no{}, 3, 0, 0, 0);
+    else if (w == 1)
+      blocks(no{}, yes{}, yes{}, 1, 0, 3, 1);
+    else if (w == 2)
+      blocks(no{}, yes{}, no{}, 2, 0, 2, 1);
+    else
+      blocks(no{}, no{}, no{}, 3, 2, 0, 0);
   }
   __syncthreads();
 
