@@ -732,7 +732,8 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   // ---- T' = T diag(beta) as hi/lo A fragments (rows i, 8 columns j), where
   // L was; V rows into the tile where kg was ----
   bf16_t *tfr = reinterpret_cast<bf16_t *>(sm.lt);  // [hi: 6 x 64 lanes x 8][lo: 6 x 64 x 8]
-  for (int x = w; x < 6; x += 4) {
+  // fragments x = w and (waves 0 and 1) x = w + 4
+  auto tprime = [&](int x) {
     const int i = SB * lt_mt(x) + nn;
     const int j0 = 32 * lt_s(x) + 8 * grp;
     const float4 t0v = *reinterpret_cast<const float4 *>(&sm.tt[sw_lt(i, j0)]);
@@ -746,7 +747,9 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
     for (int e = 0; e < 8; ++e) split_bf16((j0 + e <= i) ? tv[e] * bw[e] : 0.f, fh, fl, e);
     *reinterpret_cast<bf16x8 *>(&tfr[(x * 64 + l) * 8]) = fh;
     *reinterpret_cast<bf16x8 *>(&tfr[((6 + x) * 64 + l) * 8]) = fl;
-  }
+  };
+  tprime(w);
+  if (w < 2) tprime(w + 4);
   bf16_t *vt = kgt;
 #pragma unroll
   for (int s = 0; s < 4; ++s)
