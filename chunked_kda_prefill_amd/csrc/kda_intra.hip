@@ -639,30 +639,28 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   const int d0 = SB * w;
   f32x4 PC;  // T_ww
   {
-    f32x4 YC, YtC, PtC;  // X = -L_ww and X^T; P = I + X and P^T
+    // The factors commute, so each one multiplies P from the left:
+    // P <- P + Z P with Z = X^2, X^4, X^8, which needs Z^T (as the A operand)
+    // and P, but never P^T: eight products.
+    f32x4 ZC, ZtC;  // X = -L_ww and its transpose
     const float4 rowv = *reinterpret_cast<const float4 *>(&sm.lt[sw_lt(d0 + nn, d0 + 4 * grp)]);
     const float rv[4] = {rowv.x, rowv.y, rowv.z, rowv.w};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * grp + r;
-      YC[r] = -Ld[r];  // already zero on and above the diagonal
-      YtC[r] = (m < nn) ? -rv[r] : 0.f;
-      PC[r] = (m == nn) ? 1.f : YC[r];
-      PtC[r] = (m == nn) ? 1.f : YtC[r];
+      ZC[r] = -Ld[r];  // already zero on and above the diagonal
+      ZtC[r] = (m < nn) ? -rv[r] : 0.f;
+      PC[r] = (m == nn) ? 1.f : ZC[r];  // P = I + X
     }
+    Split4 sZ = split4(ZC), sZt = split4(ZtC);
 #pragma unroll
     for (int it = 0; it < 3; ++it) {
-      const Split4 sY = split4(YC), sYt = split4(YtC), sPt = split4(PtC);
-      const f32x4 Y2C = mm16s(sYt, sY, zero4());   // Y Y
-      const Split4 sY2 = split4(Y2C);
-      const f32x4 PnC = mm16s(sPt, sY2, PC);       // P + P Y^2
-      if (it < 2) {
-        const f32x4 Y2tC = mm16s(sY, sYt, zero4());  // Y^T Y^T
-        PtC = mm16s(sY2, sPt, PtC);                  // P^T + (Y^2)^T P^T
-        YC = Y2C;
-        YtC = Y2tC;
-      }
-      PC = PnC;
+      // Z^T <- Z^T Z^T, and Z <- Z Z (not needed after the last step)
+      const f32x4 Z2tC = mm16s(sZ, sZt, zero4());
+      const Split4 sZ2t = split4(Z2tC);
+      if (it < 2) sZ = split4(mm16s(sZt, sZ, zero4()));
+      sZt = sZ2t;
+      PC = mm16s(sZt, split4(PC), PC);  // P + Z P
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.tt[sw_lt(d0 + 4 * grp + r, d0 + nn)] = PC[r];
