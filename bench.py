@@ -10,6 +10,13 @@ with HIP events on the launch stream, on every EVENT_STRIDE-th step only: a
 timing event costs ~3.5 us of stream time on this device, and three per
 step would slow the very throughput being measured by ~10%.
 
+Before the W warmup steps, untimed steps run for --settle-seconds of wall
+time (default 0.3 s): this device takes tens of milliseconds of sustained
+load to reach its steady clocks, and a 100-step window that starts after 20
+warmup steps reads ~10% slower than one after 300 (110.9 vs 100.7 us per
+headline step, measured back to back on one box).  The timed region is
+still exactly K steps; the settle time and its step count are reported.
+
 Inputs are resident in HBM before timing starts.  Several device copies of
 the inputs are rotated so that every step reads inputs that are not left in
 the 256 MB Infinity Cache by the previous step.
@@ -43,6 +50,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-seconds", type=float, default=0.3,
+                    help="untimed steps for this long before the warmup steps (device clocks)")
     ap.add_argument("--workload", default="headline",
                     help="headline | tiny | batchB | sharegpt | long")
     ap.add_argument("--rotate", type=int, default=0,
@@ -336,6 +345,15 @@ def main():
     f_check = fin.clone()
     del o_ref, f_ref
 
+    # settle: untimed steps until the device has run under load for
+    # --settle-seconds (its clocks reach their steady state), then W warmup steps
+    settle_steps = 0
+    t_settle = time.perf_counter() + max(0.0, args.settle_seconds)
+    while time.perf_counter() < t_settle:
+        for _ in range(10):
+            step(sets[settle_steps % R])
+            settle_steps += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(sets[i % R])
     torch.cuda.synchronize()
@@ -465,7 +483,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": T, "N": N, "H": H, "K": 128, "V": 128, "BT": 64,
                    "SB": 16, "chunks": nc, "initial_state": w.initial_state is not None,
-                   "input_copies_rotated": R},
+                   "input_copies_rotated": R,
+                   "settle": {"seconds": args.settle_seconds, "steps": settle_steps}},
         "roofline": roofline, "path": path, "cpu_baseline": cpu, "parity_vs_oracle": parity,
         "gpu": torch.cuda.get_device_name(dev),
     }
