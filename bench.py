@@ -109,7 +109,8 @@ def sweep(args, torch, np, kda, wl):
     calls, then 100 calls, each after an untimed read of a 512 MiB device
     buffer that evicts L2 and the MALL (a read, so that no dirty lines are
     left to write back during the call), bracketed by HIP events on the
-    call's stream.
+    call's stream.  The device copy that gives the bandwidth ceiling runs
+    after --settle-seconds of copies.
     Prints a markdown table: median / p10 / p90, tokens/s, algorithmic GB/s
     and TFLOP/s, the fraction of 8 TB/s, and the fp64 oracle's rate on a
     bounded sample (a few heads) of the same inputs.  Decode configs are
@@ -131,8 +132,14 @@ def sweep(args, torch, np, kda, wl):
     # achievable ceiling: a plain device copy of 1 GiB
     a = torch.ones(2**28, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
+    # settle the device's clocks under load first (see --settle-seconds)
+    t_settle = time.perf_counter() + max(0.0, args.settle_seconds)
+    while True:
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_settle:
+            break
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(10):
