@@ -449,6 +449,19 @@ def main():
             "TFLOP/s": round(path_flops / step_s / 1e12, 2),
             "mfma_frac": round(path_flops / step_s / 1e12 / BF16_PEAK_TFLOPS, 4),
             "step_us": step_dist}
+    # secondary bounds: the path's bytes at 8 TB/s, its FLOP at the bf16 MFMA
+    # peak, its exponentials (two per (token, head, key channel) in the intra
+    # kernel) at the transcendental rate (a quarter of the fp32 lane rate:
+    # 1,024 SIMDs x 4 per clock x 2.4 GHz), and the serial chain: the longest
+    # (sequence, head) chain's chunk count and the recurrence time per chunk
+    lens = np.diff(w.cu_seqlens.astype(np.int64))
+    chain = int(((lens + 63) // 64).max()) if len(lens) else 0
+    path["bounds_us"] = {
+        "hbm": round(path_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+        "mfma_bf16": round(path_flops / (BF16_PEAK_TFLOPS * 1e12) * 1e6, 2),
+        "transcendental": round(2 * T * H * 128 / (1024 * 4 * 2.4e9) * 1e6, 2),
+        "chain_chunks": chain,
+        "recurrence_us_per_chunk": round(rec_us / chain, 3) if chain else None}
 
     # --- CPU baseline: the fp64 oracle on a bounded sample -----------------
     cpu = None
@@ -470,8 +483,15 @@ def main():
         cpu_s = time.process_time() - cpu0
         wall = float(np.median(walls))
         frac = len(hsel) / H
+        cpu_model = None
+        try:
+            with open("/proc/cpuinfo") as fh:
+                cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh
+                                  if ln.startswith("model name")), None)
+        except OSError:
+            pass
         cpu = {"value": round(T * frac / wall, 1), "unit": "tokens/s", "cores": threads,
-               "kind": "oracle",
+               "cpu_model": cpu_model, "kind": "oracle",
                "sample": f"{w.name}: all {T} tokens x {len(hsel)} of {H} heads, run {len(walls)}x "
                          f"({cpu_s:.1f} CPU-s in total); median {wall:.3f} s wall per run"
                          + ("" if frac == 1 else "; tokens/s scaled to all heads")}
