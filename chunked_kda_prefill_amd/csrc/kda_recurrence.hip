@@ -158,9 +158,19 @@ __device__ __forceinline__ int o_stage_off(int p) {
 
 // Byte offset, within a staged o row, of the 4 columns VCOL(nt, 4 grp) ..
 // + 3 (value tile nt of part p), and the output column of staged piece k.
+// The staged pieces of a row are XOR-permuted by the row: the 16 rows one
+// lane group writes (one piece each) are O_ROW bytes apart, so without it
+// every 256 / O_ROW-th row would hit the same LDS banks.
 template <class C>
-__device__ __forceinline__ int o_stage_col(int nt, int grp, int p) {
-  return C::TILES == 1 ? 8 * grp : 2 * (VCOL(nt, 4 * grp) - 16 * C::TILES * p);
+__device__ __forceinline__ int o_stage_swz(int row) {
+  constexpr int PER_ROW = C::O_ROW / C::PIECE;
+  return (row / (256 / C::O_ROW)) % PER_ROW;
+}
+template <class C>
+__device__ __forceinline__ int o_stage_col(int nt, int grp, int p, int row) {
+  const int off = C::TILES == 1 ? 8 * grp : 2 * (VCOL(nt, 4 * grp) - 16 * C::TILES * p);
+  const int piece = off / C::PIECE;
+  return ((piece ^ o_stage_swz<C>(row)) * C::PIECE) | (off % C::PIECE);
 }
 template <class C>
 __device__ __forceinline__ int o_piece_col(int k, int p) {
@@ -191,7 +201,7 @@ __device__ __forceinline__ void store_o_staged(const RecurArgs &a, const uint8_t
 #pragma unroll
   for (int k = 0; k < OStore<C, NCP>::STORES; ++k) {
     const int i = (k * NCP + cw) * 64 + l;
-    const int row = i / PER_ROW, piece = i % PER_ROW;
+    const int row = i / PER_ROW, piece = (i % PER_ROW) ^ o_stage_swz<C>(row);
     const int off = row * row_bytes + 2 * o_piece_col<C>(piece, p);
     if (C::PIECE == 16) {
       const u32x4 v = *reinterpret_cast<const u32x4 *>(src + i * 16);
@@ -607,7 +617,8 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int q = 0; q < TPW; ++q)
-          *reinterpret_cast<bf16x4 *>(ost + (16 * mt + nn) * C::O_ROW + o_stage_col<C>(nt0 + q, grp, p)) =
+          *reinterpret_cast<bf16x4 *>(ost + (16 * mt + nn) * C::O_ROW +
+                                      o_stage_col<C>(nt0 + q, grp, p, 16 * mt + nn)) =
               o_pend[mt][q];
     }
     o_t0 = t0;
