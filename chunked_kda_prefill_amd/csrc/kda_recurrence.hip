@@ -504,14 +504,19 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
 
     // v_new starts from U (C layout: [token][value]); o^T from zero
     f32x4 vn[4][TPW], ot[4][TPW];
+    // one 16-byte read per token tile pair (both C tiles of the pair, in
+    // the lane's own 16 bytes: contiguous across lanes, no bank conflicts)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
       for (int q = 0; q < TPW; ++q) {
-        const bf16x4 u = *reinterpret_cast<const bf16x4 *>(blk + U_OFFSET(nt0 + q, mt, l));
+        const bf16x8 u = *reinterpret_cast<const bf16x8 *>(blk + U_OFFSET(nt0 + q, 2 * mp, l));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vn[mt][q][r] = rd.use_u ? (float)u[r] : 0.f;
-        ot[mt][q] = zero4();
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vn[2 * mp + m][q][r] = rd.use_u ? (float)u[4 * m + r] : 0.f;
+          ot[2 * mp + m][q] = zero4();
+        }
       }
 
     // the state is no longer needed unscaled: apply Diag(gamma) now, while
