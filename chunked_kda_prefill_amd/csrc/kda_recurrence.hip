@@ -234,6 +234,62 @@ __device__ __forceinline__ void copy_share(const uint8_t *src, uint8_t *dst, int
     copy_range<C, HALF, C::ROUNDS>(r, lbase, p, l);
 }
 
+// Touch of a block two chunks ahead: one dword of every PARTS-th 128-byte
+// line of the block (offset by the part), loaded by LDS DMA into a 256-byte
+// sink that nobody reads.  The lines land in the XCD's L2, which the parts
+// of a chain share, so that the block's copy one chunk later hits there
+// instead of waiting on HBM.  Lanes past the block fail the buffer
+// resource's range check.  Copy wave CW issues touches [K0, K1).
+template <class C, int CW>
+struct Touch {
+  static constexpr int LINES = (BLOCK_BYTES / 128 + C::PARTS - 1) / C::PARTS;  // per part
+  static constexpr int TOTAL = (LINES + 63) / 64;  // one line per lane
+  static constexpr int K0 = CW == 0 ? 0 : (TOTAL + 1) / 2;
+  static constexpr int K1 = CW == 0 ? (TOTAL + 1) / 2 : TOTAL;
+  static constexpr int N = K1 - K0;  // touch instructions of this wave per block
+};
+template <class C, int CW>
+__device__ __forceinline__ void touch_share(const uint8_t *src, uint32_t sink, int p, int l) {
+  const __amdgpu_buffer_rsrc_t r = block_rsrc(src);
+#pragma unroll
+  for (int k = Touch<C, CW>::K0; k < Touch<C, CW>::K1; ++k) {
+    const uint32_t voff = ((k * 64 + l) * C::PARTS + p) * 128;
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+        "buffer_load_dword %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(r), "s"(sink)
+        : "memory");
+  }
+}
+__device__ __forceinline__ constexpr int vmcnt_imm(int n) {
+  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4);  // vmcnt n, expcnt any, lgkmcnt 0
+}
+// Copy wave CW before chunk c's barrier: chunk c's copy is complete.  Issued
+// after it, in order, and free to stay outstanding: the touch of chunk c + 1
+// (`touch`) and the o stores of chunk c - 2 (`stores`).
+template <class C, int NCP, int CW>
+__device__ __forceinline__ void wait_copy(bool touch, bool stores) {
+  constexpr int N = Touch<C, CW>::N, S = OStore<C, NCP>::STORES;
+  static_assert(N + S < 64, "fits the vmcnt field");
+  if (touch && stores)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(N + S));
+  else if (touch)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+  else if (stores)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(S));
+  else
+    __builtin_amdgcn_s_waitcnt(0);
+}
+template <class C, int NCP>
+__device__ __forceinline__ void touch_block(const uint8_t *src, uint32_t sink, int cw, int p, int l) {
+  if (cw == 0)
+    touch_share<C, 0>(src, sink, p, l);
+  else
+    touch_share<C, 1>(src, sink, p, l);
+}
+
 // What one workgroup group computes: a whole chain (segments == 1), or one
 // run of a segment of a chain (the two phases of chunk-parallel state
 // passing, kda_recurrence.h).
@@ -353,6 +409,7 @@ template <int NC, int NCP, int TPW, bool SEG>
 __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a) {
   using C = RecCfg<NC, NCP, TPW>;
   __shared__ __align__(16) uint8_t lds[2][BLOCK_BYTES];
+  __shared__ __align__(16) uint8_t touch_sink[256];  // written by the touches, never read
   const int b = blockIdx.x;
   const int xcd = b & 7, i = b >> 3;
   // run index: a chain, or (segments > 1) one run of a chain's segment
@@ -392,23 +449,27 @@ __global__ __launch_bounds__(64 * (NC + NCP)) void recurrence_kernel(RecurArgs a
   const uint8_t *chain_blocks = a.blocks + (int64_t)h * nc_max * BLOCK_BYTES;
 
   if (NCP > 0 && w >= NC) {
-    // ---- copy waves: chunk c+1's block while chunk c is computed, and
-    // the o of chunk c-1 (staged in LDS by the compute waves) to memory ----
-    // Each iteration issues the copy, then the stores; the wait at the top
-    // of the next one covers the copy but not the stores issued after it
-    // (vector memory operations complete in order).
+    // ---- copy waves: chunk c+1's block while chunk c is computed, the
+    // touch of chunk c+2's, and the o of chunk c-1 (staged in LDS by the
+    // compute waves) to memory ----
+    // Each iteration issues the copy, the touch, then the stores; the wait
+    // at the top of the next one covers the copy but not what was issued
+    // after it (vector memory operations complete in order).
     const int cw = w - NC;
+    const uint32_t sink = lds_base_of(touch_sink);
     if (c_beg < c_end) copy_share<C, NCP>(chain_blocks + c_beg * BLOCK_BYTES, lds[0], cw, p, l);
+    if (c_beg + 1 < c_end) touch_block<C, NCP>(chain_blocks + (c_beg + 1) * BLOCK_BYTES, sink, cw, p, l);
     for (int64_t c = c_beg; c < c_end; ++c) {
-      // the copy of this chunk is complete; o stores issued after it may not be
-      if (c > c_beg + 1 && rd.write_o)
-        __builtin_amdgcn_s_waitcnt(OStore<C, NCP>::STORES | (0x7 << 4));
+      const bool touch = c + 1 < c_end, stores = c > c_beg + 1 && rd.write_o;
+      if (cw == 0)
+        wait_copy<C, NCP, 0>(touch, stores);
       else
-        __builtin_amdgcn_s_waitcnt(0);
+        wait_copy<C, NCP, 1>(touch, stores);
       __syncthreads();
       const int cur = (int)((c - c_beg) & 1);
       if (c + 1 < c_end)
         copy_share<C, NCP>(chain_blocks + (c + 1) * BLOCK_BYTES, lds[cur ^ 1], cw, p, l);
+      if (c + 2 < c_end) touch_block<C, NCP>(chain_blocks + (c + 2) * BLOCK_BYTES, sink, cw, p, l);
       if (c > c_beg && rd.write_o) store_o_staged<C, NCP>(a, lds[cur ^ 1], c - 1, h, p, cw, l);
     }
     __syncthreads();  // the compute waves have staged the last chunk's o
