@@ -233,8 +233,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t unit_rsrc(const void *base, in
   return uniform_rsrc(p, n * H * DK * elem);
 }
 
-// bf16 rows are read 16 bytes per lane: for key slab s (32 channels) lane
-// group grp reads the 4-channel groups 2m and 2m+1, m = load_m(grp), and a
+// The factor phase reads bf16 rows 16 bytes per lane from the staged q and
+// k tiles: for key slab s (32 channels) lane group grp reads the 4-channel
+// groups 2m and 2m+1, m = load_m(grp), and a
 // permlane16 swap between lane groups (0,1) and (2,3) turns them into the
 // groups grp and grp + 4 that the channel slots hold (slot_ch(2s, grp) and
 // slot_ch(2s + 1, grp)).
@@ -246,13 +247,22 @@ __device__ __forceinline__ void slab_to_slots(const u32x4 &raw, uint2 &lo, uint2
   hi = make_uint2(a.y, b.y);
 }
 
-// Inputs of one (chunk, head) unit for one lane: row `row`, the channel
-// slots of kda_cumsum.h (q and k as loaded: slab_to_slots() gives the
-// slots).  Loaded into registers ahead of use.
+// Whole-row loads of bf16 tensors: load s of wave w covers rows
+// whole_row(w, s, l) = 16 w + 4 s + l / 16, 16 bytes per lane at channel
+// 8 (l % 16) + 0..7, so one instruction reads four 256-byte rows.  That
+// streams faster than loading the channel-slot layout directly, which gives
+// each instruction 16 rows x 64 bytes (headline launch 66.6 -> 62.9 us for V
+// alone).  The rows reach the slot layout through LDS: V through the V tile
+// U reads, q and k through the wave's own rows of x (see intra_unit).
+__device__ __forceinline__ int whole_row(int w, int s, int l) { return SB * w + 4 * s + (l >> 4); }
+
+// Inputs of one (chunk, head) unit for one lane: the channel slots of
+// kda_cumsum.h for g and beta (row `row`), q and k as whole rows (see
+// whole_row).  Loaded into registers ahead of use.
 struct UnitInputs {
   int64_t t0;
   int n;
-  u32x4 q[4], k[4];  // per key slab: channels 32 s + 8 load_m(grp) + 0..7
+  u32x4 q[4], k[4];  // load s: row whole_row(w, s, l), channels 8 (l % 16) + 0..7
   float4 g[8];       // channels slot_ch(j, grp) + 0..3
   uint32_t beta;     // bits: fp32 beta, or bf16 beta logit (zero-extended)
 };
@@ -287,34 +297,35 @@ __device__ __forceinline__ void load_unit(const IntraArgs &a, const int4 info, i
       in.beta = __builtin_amdgcn_raw_buffer_load_b32(rb, 4 * row * a.H, 0, AUX_G);
     }
   }
+  // q and k as whole rows (see whole_row): wave wr = row / 16, lane lr
+  const int wr = row >> 4, lr = (grp << 4) | (row & 15);
   if (part < 0 || part == 1) {
     const __amdgpu_buffer_rsrc_t rq = unit_rsrc(a.q, tb, n, a.H, h, 2);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      in.q[s] = __builtin_amdgcn_raw_buffer_load_b128(rq, 2 * (roff + 32 * s + 8 * load_m(grp)), 0,
-                                                      AUX_QK);
+      in.q[s] = __builtin_amdgcn_raw_buffer_load_b128(
+          rq, 2 * (whole_row(wr, s, lr) * a.H * DK + 8 * (lr & 15)), 0, AUX_QK);
   }
   if (part < 0 || part == 2) {
     const __amdgpu_buffer_rsrc_t rk = unit_rsrc(a.k, tb, n, a.H, h, 2);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      in.k[s] = __builtin_amdgcn_raw_buffer_load_b128(rk, 2 * (roff + 32 * s + 8 * load_m(grp)), 0,
-                                                      AUX_QK);
+      in.k[s] = __builtin_amdgcn_raw_buffer_load_b128(
+          rk, 2 * (whole_row(wr, s, lr) * a.H * DK + 8 * (lr & 15)), 0, AUX_QK);
   }
 }
 
 
-// V rows of the lane (needed only for U, so loaded late), 16 bytes per
-// key slab: channels 32 s + 8 load_m(grp) + 0..7.  Rows past n are zeroed
-// where they are used.
-__device__ __forceinline__ void load_v(const IntraArgs &a, int64_t t0, int n, int h, int row,
-                                       int grp, u32x4 (&v)[4]) {
+// V rows of wave w as whole rows (needed only for U, so loaded late).  Rows
+// past n read as zeros (see unit_rsrc).
+__device__ __forceinline__ void load_v(const IntraArgs &a, int64_t t0, int n, int h, int w, int l,
+                                       u32x4 (&v)[4]) {
   const int64_t tb = t0 < a.T ? t0 : a.T - 1;
-  const int roff = row * a.H * DK;
   const __amdgpu_buffer_rsrc_t rv = unit_rsrc(a.v, tb, n, a.H, h, 2);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
-    v[s] = __builtin_amdgcn_raw_buffer_load_b128(rv, 2 * (roff + 32 * s + 8 * load_m(grp)), 0, AUX_V);
+    v[s] = __builtin_amdgcn_raw_buffer_load_b128(
+        rv, 2 * (whole_row(w, s, l) * a.H * DK + 8 * (l & 15)), 0, AUX_V);
 }
 
 // One (chunk, head) unit whose inputs are already in `nxt` (loads issued).
@@ -373,6 +384,18 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
                        : __uint_as_float(in.beta);
   __syncthreads();
 
+  // ---- q and k rows into the wave's own 8 KB of x (bf16 [16][128] each),
+  // to be read back in the load layout by the factor phase.  Every wave has
+  // finished the previous unit (whose U and W read x) at the barrier above,
+  // and nobody but this wave touches these rows of x until its k~ writes. ----
+  bf16_t *qst = reinterpret_cast<bf16_t *>(sm.x) + 2 * SB * DK * w;
+  bf16_t *kst = qst + SB * DK;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    *reinterpret_cast<u32x4 *>(&qst[sw_bf16(whole_row(0, s, l), 8 * (l & 15))]) = in.q[s];
+    *reinterpret_cast<u32x4 *>(&kst[sw_bf16(whole_row(0, s, l), 8 * (l & 15))]) = in.k[s];
+  }
+
   // ---- per-channel tables (two threads per channel) ----
   {
     const int ch = tid & (DK - 1);
@@ -408,12 +431,15 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   // Aqk^T block (w, b): lane holds [j = 16b + 4grp + r][i = 16w + nn]; it is
   // half (b & 1) of the recurrence's Aqk fragment (mt = w, s = b >> 1).
   // L block (w, b): lane holds [i = 16w + 4grp + r][j = 16b + nn] * beta_i.
-  // q and k in the channel slots (their loads are waited for here)
+  // q and k in the channel slots: row nn of the staged tiles, channels
+  // 32 s + 8 load_m(grp) + 0..7, then slab_to_slots()
   uint2 qs[8], ks[8];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    slab_to_slots(in.q[s], qs[2 * s], qs[2 * s + 1]);
-    slab_to_slots(in.k[s], ks[2 * s], ks[2 * s + 1]);
+    const u32x4 qr = *reinterpret_cast<const u32x4 *>(&qst[sw_bf16(nn, 32 * s + 8 * load_m(grp))]);
+    const u32x4 kr = *reinterpret_cast<const u32x4 *>(&kst[sw_bf16(nn, 32 * s + 8 * load_m(grp))]);
+    slab_to_slots(qr, qs[2 * s], qs[2 * s + 1]);
+    slab_to_slots(kr, ks[2 * s], ks[2 * s + 1]);
   }
   // fused prologue: the row's L2 norms (its 128 channels are spread over the
   // lanes nn, nn + 16, nn + 32 and nn + 48; the two swap-and-add steps give
@@ -623,7 +649,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
 
   // ---- this unit's V (only U needs it, at the end) ----
   u32x4 vrow[4];
-  load_v(a, t0, n, h, row, grp, vrow);
+  load_v(a, t0, n, h, w, l, vrow);
 
   // ---- kg and K*Gamma rows into bf16 tiles where k~ was ----
   bf16_t *kgt = reinterpret_cast<bf16_t *>(sm.x);
@@ -755,7 +781,7 @@ __device__ __forceinline__ void intra_unit(const IntraArgs &a, IntraSmem &sm, in
   bf16_t *vt = kgt;
 #pragma unroll
   for (int s = 0; s < 4; ++s)
-    *reinterpret_cast<u32x4 *>(&vt[sw_bf16(row, 32 * s + 8 * load_m(grp))]) = vrow[s];
+    *reinterpret_cast<u32x4 *>(&vt[sw_bf16(whole_row(w, s, l), 8 * (l & 15))]) = vrow[s];
   __syncthreads();
 
   auto th = [&](int x) { return *reinterpret_cast<const bf16x8 *>(&tfr[(x * 64 + l) * 8]); };
