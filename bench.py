@@ -140,17 +140,24 @@ def sweep(args, torch, np, kda, wl):
         torch.cuda.synchronize()
         if time.perf_counter() >= t_settle:
             break
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(10):
-        b.copy_(a)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 10 * 2 * a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    def stream_gbs(fn, bytes_per_call):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        e0.record(stream)
+        for _ in range(10):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return 10 * bytes_per_call / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    nb = a.numel() * 4
+    copy_gbs = stream_gbs(lambda: b.copy_(a), 2 * nb)            # the runtime's copy
+    ew_gbs = stream_gbs(lambda: torch.mul(a, 1.0, out=b), 2 * nb)  # an elementwise kernel
     del a, b
     threads = oracle.max_threads()
     print(f"Device copy of 1 GiB (read + write): {copy_gbs:.0f} GB/s "
-          f"({copy_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s). Oracle threads: {threads}.\n")
+          f"({copy_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s) through the runtime's copy, "
+          f"{ew_gbs:.0f} GB/s ({ew_gbs / HBM_PEAK_GBS:.1%}) through an elementwise kernel "
+          f"(x * 1). Oracle threads: {threads}.\n")
     print("| config | T | N | H | chunks | median µs | p10 µs | p90 µs | M tokens/s | GB/s | "
           "HBM frac | TFLOP/s | oracle tokens/s (heads) | GPU/oracle |")
     print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
