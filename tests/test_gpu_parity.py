@@ -176,6 +176,27 @@ def test_varlen_bit_exact(dev):
     assert np.array_equal(o, o2) and np.array_equal(f, f2)
 
 
+@pytest.mark.parametrize("H", [8, 16, 32], ids=["one_wave_parts8", "two_waves_parts4",
+                                                  "four_waves_parts2"])
+def test_short_chains_in_each_launch_configuration(dev, H):
+    # 4 sequences of 2, 1, 1 and 3 chunks: 32, 64 and 128 chains put the
+    # recurrence in its one-, two- and four-compute-wave configurations (8, 4
+    # and 2 workgroups per chain), where the copy waves' block copies and L2
+    # touches run out after one to three chunks.  Against the oracle, and
+    # bitwise against each sequence alone (H chains: the one-wave
+    # configuration), since the per-column arithmetic does not depend on how
+    # the value tiles are grouped.
+    w = wl.small([100, 64, 3, 150], H=H, seed=46, h0="normal")
+    log(f"[case] short chains H={H} ({4 * H} chains)")
+    o, f = run_gpu(w, dev)
+    parity(o, f, *run_oracle(w), f"short chains H={H}")
+    cu = w.cu_seqlens
+    for s in range(w.N):
+        os_, fs = run_gpu(_sub(w, [s]), dev)
+        assert np.array_equal(os_, o[cu[s]:cu[s + 1]]), (H, s)
+        assert np.array_equal(fs[0], f[s]), (H, s)
+
+
 def test_null_initial_state_equals_zeros(dev):
     w = wl.small([100, 37], H=2, seed=44, h0="zeros")
     log("[case] NULL initial_state vs zeros")
