@@ -197,6 +197,22 @@ def test_short_chains_in_each_launch_configuration(dev, H):
         assert np.array_equal(fs[0], f[s]), (H, s)
 
 
+@pytest.mark.parametrize("bval", [0.0, 1.0], ids=["beta_0", "beta_1"])
+def test_degenerate_beta(dev, bval):
+    # beta = 0: L = 0, T = I, W = U = 0, so v_new = 0, the state only decays
+    # and o reads the decayed initial state; beta = 1 on every token: the
+    # strongest correction the delta rule applies.  Ragged lengths, a normal
+    # initial state, g down to its lower bound.
+    base = wl.small([130, 64, 17, 200], H=4, seed=47, h0="normal", pinned_fraction=0.5)
+    beta = np.full_like(base.beta, bval)
+    w = wl.Workload(name=base.name + f"_beta{bval:g}", seed=base.seed, q=base.q, k=base.k,
+                    v=base.v, g=base.g, beta=beta, initial_state=base.initial_state,
+                    cu_seqlens=base.cu_seqlens, scale=base.scale)
+    log(f"[case] beta = {bval:g}")
+    o, f = run_gpu(w, dev)
+    parity(o, f, *run_oracle(w), f"beta={bval:g}")
+
+
 def test_null_initial_state_equals_zeros(dev):
     w = wl.small([100, 37], H=2, seed=44, h0="zeros")
     log("[case] NULL initial_state vs zeros")
